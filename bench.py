@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Throughput of the tree-verify MLA-absorb attention step on one MI355X.
+
+One step = one pass of the whole hot path over one batch of trees:
+  tv_tree_rope    rotate the queries and the tree's own key rows at
+                  prefix + depth (float64 angles), in place, then
+  tv_verify_attn  prefix + ancestor masked softmax attention in the absorbed
+                  latent space, writing out [B, q_len, H, d_c].
+The prefix key rows are rotated once before timing (the cache holds keys
+rotated when they were written).  Inputs are seeded synthetic tensors already
+resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  `value` is steps (verify calls) per second.  The
+`roofline` object is for the attention kernel, timed with HIP events on the
+stream it runs on; `cpu_baseline` times the float64 CPU oracle on a bounded
+sample of the same workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn calls/sec + achieved HBM GB/s (% roofline) at B,H,prefix,budget"
+HBM_PEAK_GBS = 8000.0
+PEAKS_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32_mfma": 157.3, "f32_valu": 157.3}
+
+# Which kernel the library runs for each cache dtype, the arithmetic it does,
+# and the roofline that bounds it.
+KERNELS = {
+    "bf16": dict(name="attn_valu_kernel", source="tree_verify_mla_tv_amd/csrc/attn_valu.hip", bound="alu",
+                 peak="f32_valu", dtype="f32"),
+    "f32": dict(name="attn_valu_kernel", source="tree_verify_mla_tv_amd/csrc/attn_valu.hip", bound="alu",
+                peak="f32_valu", dtype="f32"),
+}
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_counts(w, parent) -> dict:
+    """Bytes and flops of the step's tensors, each touched once (per call)."""
+    import numpy as np
+    kvb = 2 if w.kv_dtype == "bf16" else 4
+    B, q, H, P, kv, dc, dr = w.B, w.q_len, w.H, w.prefix_len, w.kv_len, w.d_c, w.d_r
+    depth = np.zeros_like(parent)
+    for b in range(B):
+        for i in range(1, q):
+            depth[b, i] = depth[b, parent[b, i]] + 1
+    visible_pairs = int(H * (P + depth + 1).sum())
+    flops = visible_pairs * (2 * (dc + dr) + 2 * dc)
+    attn_bytes = (B * q * H * dc * 4 + B * q * H * dr * 4 + B * kv * dc * kvb + B * kv * dr * kvb
+                  + B * q * 4 + B * q * H * dc * 4)
+    rope_bytes = 2 * (B * q * H * dr * 4 + B * q * dr * kvb) + B * q * 4
+    return dict(visible_pairs=visible_pairs, flops=flops, attn_bytes=attn_bytes, rope_bytes=rope_bytes,
+                step_bytes=attn_bytes + rope_bytes)
+
+
+def cpu_baseline(inp, w, n_sample: int) -> dict:
+    """The oracle as it stands, on the first n_sample trees of the same batch."""
+    import threadpoolctl
+    from oracle import tv_oracle as O
+    s = slice(0, n_sample)
+    t0 = time.perf_counter()
+    O.verify_step(inp["q_lat"][s], inp["q_rope"][s], inp["c_kv"][s], inp["k_rope"][s], inp["parent"][s],
+                  w.prefix_len, w.theta, w.sm_scale, w.kv_dtype)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] or [1])
+    return {"value": round(1.0 / (dt * w.B / n_sample), 6), "unit": "calls/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle (RoPE + attention) on {n_sample} of {w.B} trees of the same batch, "
+                      f"{dt:.2f} s, scaled x{w.B / n_sample:g} to one call; host CPUs available: "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def load_traffic(kernel: dict, workload: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(kernel["source"]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-sample", type=int, default=6, help="trees the CPU oracle times (0 = skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the verify "
+              f"step shards over batch entries with no exchange, so the one-GPU figure is one shard's "
+              f"throughput.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from tree_verify_mla_tv_amd import tv
+    from tree_verify_mla_tv_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload or W.SERVING]
+    tv.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(w)
+
+    def cache(a):
+        if w.kv_dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q_lat = torch.from_numpy(inp["q_lat"]).to(dev)
+    q_rope = torch.from_numpy(inp["q_rope"]).to(dev)
+    c_kv = cache(inp["c_kv"])
+    k_rope = cache(inp["k_rope"])
+    parent = torch.from_numpy(inp["parent"]).to(dev)
+    P = w.prefix_len
+    if P > 0:
+        tv.rope_neox(k_rope[:, :P, :], None, w.theta)  # cache fill, outside the timed region
+    out = torch.empty_like(q_lat)
+    dt_code = tv.TV_BF16 if w.kv_dtype == "bf16" else tv.TV_F32
+    ws_bytes = tv.workspace_size(w.B, w.H, w.q_len, P, w.d_c, w.d_r, dt_code)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev0=None, ev1=None):
+        tv.tree_rope(q_rope, k_rope, parent, P, w.theta)
+        if ev0 is not None:
+            ev0.record()
+        tv.verify_attn(q_lat, q_rope, c_kv, k_rope, parent, P, w.sm_scale, out=out, workspace=ws)
+        if ev1 is not None:
+            ev1.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    counts = algorithmic_counts(w, inp["parent"])
+    kern = KERNELS[w.kv_dtype]
+    achieved_tflops = counts["flops"] / (attn_ms * 1e-3) / 1e12
+    peak = PEAKS_TFLOPS[kern["peak"]]
+    traffic = load_traffic(kern, w.name)
+    value = 1e3 / ms_per_step
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": kern["dtype"],
+        "data": "synthetic (seeded N(0,1) inputs, random trees; no dataset or weights)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "prefix": P, "budget": w.q_len - 1,
+                   "q_len": w.q_len, "kv_len": w.kv_len, "d_c": w.d_c, "d_r": w.d_r, "kv_cache": w.kv_dtype,
+                   "tree": w.tree},
+        "hbm_gbs": round(counts["step_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(counts["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": kern["name"],
+            "bound": kern["bound"],
+            "achieved": round(achieved_tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / peak, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(attn_ms, 5),
+            "algorithmic_flops": counts["flops"],
+            "algorithmic_bytes": counts["attn_bytes"],
+            "achieved_hbm_gbs": round(counts["attn_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
+        },
+    }
+    if args.cpu_sample > 0:
+        rec["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_sample, w.B))
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

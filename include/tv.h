@@ -1,0 +1,159 @@
+/*
+ * tv.h — C ABI of libtv.so: tree-verify MLA-absorb attention on MI355X (gfx950).
+ *
+ * Pages cited (title, then section):
+ *   [RoPE page]   "Precision as Correctness: The Float64 RoPE Decision in a
+ *                 Custom CUDA Inference Engine"
+ *   [Verify page] "The Precision Imperative: Validating Numerical Accuracy in a
+ *                 Custom CUDA Attention Kernel"
+ *   [Golden page] "The Golden Reference: A Pivotal Moment in Building a Native
+ *                 DDTree Inference Engine"
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or keeps caller memory, and holds no global mutable
+ *     state: concurrent calls on different streams are safe.
+ *   - Calls are asynchronous: work is enqueued on `stream` (NULL = the null
+ *     stream) and nothing is synchronised.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are checked on the host before anything is launched; a bad
+ *     argument returns TV_ERR_INVALID (malformed) or TV_ERR_UNSUPPORTED (well
+ *     formed but outside what the kernels implement) and launches nothing.
+ *     TV_ERR_LAUNCH reports a failed kernel launch.  No C++ exception crosses
+ *     the ABI.
+ *   - Tensors are dense and row-major with the shapes given below, and every
+ *     pointer is 16-byte aligned.
+ *   - The tree of each batch entry is a parent array parent[b][0..q_len):
+ *     node 0 is the root (parent -1) and every other node's parent is an
+ *     earlier node (0 <= parent[i] < i).  Node m's key/latent row sits at kv
+ *     index prefix_len + m, so kv_len = prefix_len + q_len (the kv_len of each
+ *     test shape on the Verify page, "The Message in Full").  A parent outside
+ *     [0, i) is not detected on the device; the kernels treat such a node as a
+ *     child of nobody (it sees the prefix and itself), so no access leaves the
+ *     buffers.
+ */
+#ifndef TV_H
+#define TV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_INVALID = 1,     /* null pointer, bad size, misaligned pointer, too small workspace */
+  TV_ERR_UNSUPPORTED = 2, /* shape or dtype outside what the kernels implement */
+  TV_ERR_LAUNCH = 3       /* a kernel launch failed (hipGetLastError) */
+} tv_status_t;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype_t;
+
+/* Largest tree: one 64-bit ancestor word per node. */
+#define TV_MAX_Q_LEN 64
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* tv_status_str(tv_status_t s);
+
+/*
+ * tv_tree_positions — rotary position of every tree node.
+ *   pos[b][i] = prefix_len + depth(i), depth(root) = 0: siblings share a
+ *   position and a chain gives prefix_len + i.  (The pages leave node
+ *   positions implicit; the Golden page, "Recursive Refinement of the Decode
+ *   Loop Design", has the engine track positions of the root and draft tokens.
+ *   Depth-based positions are the reading under which a chain tree is exactly
+ *   causal decoding.)
+ *   parent [B][q_len] int32 (device), pos [B][q_len] int32 (device, written).
+ *   1 <= q_len <= TV_MAX_Q_LEN, B >= 1, prefix_len >= 0.
+ */
+tv_status_t tv_tree_positions(const int32_t* parent, int32_t B, int32_t q_len, int32_t prefix_len,
+                              int32_t* pos, hipStream_t stream);
+
+/*
+ * tv_rope_neox — in-place NeoX rotary embedding with float64 angles.
+ *   [RoPE page, "The Message", "The Float64 Decision", "What Input Knowledge
+ *   Is Required" item 1]
+ *   x is viewed as [n_seq][n_tok][n_head][d_r] elements of `dtype` with element
+ *   strides seq_stride (between sequences) and tok_stride (between tokens);
+ *   heads are contiguous rows of d_r elements.  Token t of sequence s turns at
+ *   position p = pos[s * pos_seq_stride + t], or p = t when pos is NULL.
+ *   For k < d_r/2 the pair (x[k], x[k + d_r/2]) turns by the angle
+ *   p * inv_freq[k], inv_freq[k] = 1 / theta^(2k/d_r); angle, cos, sin and the
+ *   rotation are float64 and the result is rounded once (nearest-even) to dtype.
+ *   d_r even, 2 <= d_r <= 128; n_seq, n_tok >= 0 (0 = nothing to do); n_head >= 1;
+ *   theta > 0.
+ */
+tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t n_seq, int32_t n_tok,
+                         int32_t n_head, int32_t d_r, int64_t seq_stride, int64_t tok_stride,
+                         int64_t pos_seq_stride, double theta, hipStream_t stream);
+
+/*
+ * tv_verify_attn — tree-verify attention in MLA absorb form.
+ *   [Verify page, "The Context: What Led to This Moment" (visibility-masked
+ *   absorb attention: scores, normalisation, weighted accumulation);
+ *   Golden page, "The Absorb Form of MLA" and "Principled Abstraction"]
+ *   For batch b, node i, head h (row r = i*H + h of the batch):
+ *     s_j   = sm_scale * (q_lat[b,i,h,:] . c_kv[b,j,:] + q_rope[b,i,h,:] . k_rope[b,j,:])
+ *     vis_j = j < prefix_len, or j - prefix_len is node i or an ancestor of i
+ *     out[b,i,h,:] = sum_j softmax_j(s over visible j) * c_kv[b,j,:]
+ *     lse[b,i,h]   = log sum_{visible j} exp(s_j)
+ *   The rope slices must already be rotated (tv_rope_neox).  The output stays
+ *   in latent space (the value up-projection is not applied).
+ *   Shapes (kv_len = prefix_len + q_len):
+ *     q_lat  [B][q_len][H][d_c] f32      q_rope [B][q_len][H][d_r] f32
+ *     c_kv   [B][kv_len][d_c] kv_dtype   k_rope [B][kv_len][d_r] kv_dtype
+ *     parent [B][q_len] int32
+ *     out    [B][q_len][H][d_c] f32      lse    [B][q_len][H] f32, or NULL
+ *   Supported (d_c, d_r, kv_dtype): d_c in {64, 128, 256, 512}, d_r in {32, 64},
+ *   kv_dtype TV_F32 or TV_BF16.  1 <= q_len <= TV_MAX_Q_LEN.
+ *   workspace: caller-owned device scratch of at least
+ *   tv_verify_attn_workspace_size(...) bytes (NULL allowed when that is 0).
+ *   out must not overlap any input.
+ */
+tv_status_t tv_verify_attn(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                           const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                           int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace tv_verify_attn / tv_verify_step need for these shapes
+ * (split-kv partial results); 0 when the launch needs none.  Depends on the
+ * shapes only, never on the device. */
+size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_t prefix_len, int32_t d_c,
+                                     int32_t d_r, tv_dtype_t kv_dtype);
+
+/*
+ * tv_tree_rope — the step's rotation: for every tree b and node i, turn the
+ *   query rows q_rope[b,i,h,:] (all heads) and the tree's own key row
+ *   k_rope[b, prefix_len+i, :] in place at position prefix_len + depth(i), as
+ *   tv_tree_positions and tv_rope_neox define them (one fused launch; the
+ *   positions never reach memory).
+ *   q_rope [B][q_len][H][d_r] f32, k_rope [B][prefix_len+q_len][d_r] kv_dtype,
+ *   parent [B][q_len] int32.  d_r even, 2 <= d_r <= 128; 1 <= q_len <= TV_MAX_Q_LEN.
+ */
+tv_status_t tv_tree_rope(float* q_rope, void* k_rope, tv_dtype_t kv_dtype, const int32_t* parent,
+                         int32_t prefix_len, int32_t B, int32_t H, int32_t q_len, int32_t d_r, double theta,
+                         hipStream_t stream);
+
+/*
+ * tv_verify_step — the whole verify step for one batch of trees:
+ *   1. tv_tree_rope (queries and the tree's own key rows, in place), then
+ *   2. tv_verify_attn on the result.
+ *   The prefix key rows k_rope[b, 0:prefix_len) are taken as already rotated
+ *   (the cache holds keys rotated when they were written).  Arguments as in
+ *   tv_verify_attn, plus theta; q_rope and k_rope are modified.
+ */
+tv_status_t tv_verify_step(const float* q_lat, float* q_rope, const void* c_kv, void* k_rope,
+                           const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                           int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, double theta, float sm_scale,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_H */

@@ -1,0 +1,127 @@
+"""The C ABI on the host: library loads, exports what include/tv.h declares,
+and rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_verify_mla_tv_amd import tv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tv.h")
+
+INV, UNS, OK = tv.TV_ERR_INVALID, tv.TV_ERR_UNSUPPORTED, tv.TV_OK
+A = 0x10000  # an aligned, never-dereferenced address: every case below fails validation first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("tv_rope_neox", "tv_verify_attn", "tv_verify_attn_workspace_size", "tv_status_str",
+              "tv_tree_positions", "tv_verify_step", "tv_tree_rope"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tv.load()
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+        assert s in tv.SIGNATURES, f"binding lacks {s}"
+
+
+def test_status_strings():
+    assert tv.status_str(OK) == "TV_OK"
+    assert "invalid" in tv.status_str(INV)
+    assert "not supported" in tv.status_str(UNS)
+    assert "launch" in tv.status_str(tv.TV_ERR_LAUNCH)
+    assert tv.status_str(99) == "TV_ERR_UNKNOWN"
+
+
+def _attn(lib, **kw):
+    a = dict(q_lat=A, q_rope=A, c_kv=A, k_rope=A, parent=A, prefix=4, B=1, H=2, q=3, d_c=64, d_r=32, dt=0,
+             scale=0.1, out=A, lse=None, ws=None, ws_n=0)
+    a.update(kw)
+    return lib.tv_verify_attn(a["q_lat"], a["q_rope"], a["c_kv"], a["k_rope"], a["parent"], a["prefix"], a["B"],
+                              a["H"], a["q"], a["d_c"], a["d_r"], a["dt"], a["scale"], a["out"], a["lse"],
+                              a["ws"], a["ws_n"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_lat=None), INV), (dict(q_rope=None), INV), (dict(c_kv=None), INV), (dict(k_rope=None), INV),
+    (dict(parent=None), INV), (dict(out=None), INV),
+    (dict(B=0), INV), (dict(H=0), INV), (dict(q=0), INV), (dict(prefix=-1), INV),
+    (dict(q=65), UNS), (dict(d_r=33), INV), (dict(d_c=100), UNS), (dict(d_r=16), UNS), (dict(dt=7), INV),
+    (dict(q_lat=A + 8), INV), (dict(c_kv=A + 4), INV), (dict(out=A + 12), INV), (dict(parent=A + 2), INV),
+    (dict(lse=A + 1), INV), (dict(scale=float("inf")), INV), (dict(scale=float("nan")), INV),
+    (dict(prefix=2**31 - 10), INV),
+])
+def test_verify_attn_rejects_before_launch(kw, code):
+    assert _attn(tv.load(), **kw) == code
+
+
+def test_workspace_too_small_is_rejected():
+    lib = tv.load()
+    # A long prefix with few rows is cut into kv splits, which need workspace.
+    need = tv.workspace_size(1, 1, 1, 5000, 512, 64, tv.TV_F32)
+    assert need > 0
+    assert _attn(lib, B=1, H=1, q=1, prefix=5000, d_c=512, d_r=64, ws=None, ws_n=0) == INV
+    assert _attn(lib, B=1, H=1, q=1, prefix=5000, d_c=512, d_r=64, ws=A, ws_n=need - 1) == INV
+    assert _attn(lib, B=1, H=1, q=1, prefix=5000, d_c=512, d_r=64, ws=A + 8, ws_n=need) == INV
+
+
+def test_workspace_size_is_a_function_of_shapes():
+    f = tv.workspace_size
+    assert f(2, 64, 9, 512, 512, 64, tv.TV_F32) == f(2, 64, 9, 512, 512, 64, tv.TV_F32)
+    assert f(1, 1, 1, 5000, 512, 64, tv.TV_F32) > 0
+    assert f(0, 1, 1, 10, 512, 64, tv.TV_F32) == 0          # invalid shape -> 0
+    assert f(1, 1, 65, 10, 512, 64, tv.TV_F32) == 0         # unsupported -> 0
+
+
+def test_rope_rejects_before_launch():
+    lib = tv.load()
+    r = lib.tv_rope_neox
+    assert r(A, 0, None, 0, 5, 1, 64, 0, 64, 0, 1e4, None) == OK          # nothing to do
+    assert r(A, 0, None, 3, 0, 1, 64, 0, 64, 0, 1e4, None) == OK
+    assert r(None, 0, None, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
+    assert r(A, 0, None, 1, 5, 1, 63, 0, 64, 0, 1e4, None) == INV
+    assert r(A, 0, None, 1, 5, 1, 256, 0, 256, 0, 1e4, None) == UNS
+    assert r(A, 0, None, 1, 5, 0, 64, 0, 64, 0, 1e4, None) == INV
+    assert r(A, 0, None, 1, 5, 1, 64, 0, 64, 0, 0.0, None) == INV
+    assert r(A, 0, None, 1, 5, 1, 64, 0, 64, 0, float("nan"), None) == INV
+    assert r(A, 2, None, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
+    assert r(A + 4, 0, None, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
+    assert r(A, 0, A + 2, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
+
+
+def test_tree_positions_rejects_before_launch():
+    lib = tv.load()
+    assert lib.tv_tree_positions(None, 1, 3, 0, A, None) == INV
+    assert lib.tv_tree_positions(A, 1, 3, 0, None, None) == INV
+    assert lib.tv_tree_positions(A, 0, 3, 0, A, None) == INV
+    assert lib.tv_tree_positions(A, 1, 65, 0, A, None) == UNS
+    assert lib.tv_tree_positions(A, 1, 3, -2, A, None) == INV
+
+
+def test_verify_step_rejects_before_launch():
+    lib = tv.load()
+    s = lib.tv_verify_step
+    assert s(A, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.0, 0.1, A, None, None, 0, None) == INV   # theta
+    assert s(A, A, A, A, A, 4, 1, 2, 70, 64, 32, 0, 1e4, 0.1, A, None, None, 0, None) == UNS  # q_len
+    assert s(A, None, A, A, A, 4, 1, 2, 3, 64, 32, 0, 1e4, 0.1, A, None, None, 0, None) == INV
+
+
+def test_tree_rope_rejects_before_launch():
+    r = tv.load().tv_tree_rope
+    assert r(A, A, 0, A, 4, 1, 2, 3, 64, 0.0, None) == INV      # theta
+    assert r(A, A, 0, A, 4, 1, 2, 65, 64, 1e4, None) == UNS     # q_len
+    assert r(A, A, 3, A, 4, 1, 2, 3, 64, 1e4, None) == INV      # dtype
+    assert r(A, A, 0, A, 4, 1, 2, 3, 63, 1e4, None) == INV      # odd d_r
+    assert r(None, A, 0, A, 4, 1, 2, 3, 64, 1e4, None) == INV
+    assert r(A, A + 4, 0, A, 4, 1, 2, 3, 64, 1e4, None) == INV  # misaligned
+    assert r(A, A, 0, A, -1, 1, 2, 3, 64, 1e4, None) == INV

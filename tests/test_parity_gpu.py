@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle.
+
+Tolerances (per output element; max_rel uses the row floor of tvcompare):
+  fp32 cache:  max_abs <= 1e-5 and max_rel <= 1e-2
+  bf16 cache:  max_rel <= 2e-2
+RoPE is compared bit for bit, allowing 1 ulp where the device's float64
+pow/sin/cos land on the other side of a rounding boundary (rare).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tv_oracle as O
+from tree_verify_mla_tv_amd import tv
+from tree_verify_mla_tv_amd import workloads as W
+from tvcompare import errors, pass_line, ulp_diff_bf16, ulp_diff_f32
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max_abs=1e-5, max_rel=1e-2), "bf16": dict(max_rel=2e-2)}
+LSE_TOL = {"f32": 2e-5, "bf16": 1e-4}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tv.load()
+
+
+def cuda_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def cuda_cache(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return cuda_f32(a)
+
+
+def cache_numpy(t, dtype):
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def check_out(tag, shape, out, lse, ref_out, ref_lse, dtype, rows=None):
+    out = out.cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        out, lse, ref_out, ref_lse = out[rows], lse[rows], ref_out[rows], ref_lse[rows]
+    e = errors(out, ref_out)
+    tol = TOL[dtype]
+    assert e["max_rel"] <= tol["max_rel"], (tag, e)
+    if "max_abs" in tol:
+        assert e["max_abs"] <= tol["max_abs"], (tag, e)
+    el = float(np.max(np.abs(lse - ref_lse)))
+    assert el <= LSE_TOL[dtype], (tag, "lse", el)
+    print(pass_line(tag, shape, e) + f" lse_abs={el:.1e}", flush=True)
+    return e
+
+
+def run_step(inp):
+    """The step as a serving engine runs it: the cache's prefix key rows were
+    rotated when they were written (done here first), then tv.verify_step
+    rotates the queries and the tree's key rows and runs the attention."""
+    w = inp["workload"]
+    dt = w.kv_dtype
+    q_lat = cuda_f32(inp["q_lat"])
+    q_rope = cuda_f32(inp["q_rope"])
+    c_kv = cuda_cache(inp["c_kv"], dt)
+    k_rope = cuda_cache(inp["k_rope"], dt)
+    parent = torch.from_numpy(inp["parent"]).cuda()
+    P = w.prefix_len
+    if P > 0:
+        tv.rope_neox(k_rope[:, :P, :], None, w.theta)
+    out, lse = tv.verify_step(q_lat, q_rope, c_kv, k_rope, parent, P, w.theta, w.sm_scale, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse, q_rope, k_rope
+
+
+def check_rope(got_q, got_k, ref, dt, max_frac=1e-4):
+    uq = ulp_diff_f32(got_q.cpu().numpy(), ref["q_rope"].astype(np.float32))
+    assert uq.max() <= 1 and (uq > 0).mean() <= max_frac, ("q_rope ulps", uq.max(), (uq > 0).mean())
+    if dt == "bf16":
+        uk = ulp_diff_bf16(cache_numpy(got_k, dt), O.f64_to_bf16_bits(ref["k_rope"]))
+    else:
+        uk = ulp_diff_f32(got_k.cpu().numpy(), ref["k_rope"].astype(np.float32))
+    assert uk.max() <= 1 and (uk > 0).mean() <= max_frac, ("k_rope ulps", uk.max(), (uk > 0).mean())
+
+
+SMALL = [n for n in W.WORKLOADS if n != W.SERVING]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_step_parity(name):
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w)
+    ref = O.verify_step(inp["q_lat"], inp["q_rope"], inp["c_kv"], inp["k_rope"], inp["parent"], w.prefix_len,
+                        w.theta, w.sm_scale, w.kv_dtype)
+    out, lse, q_rope, k_rope = run_step(inp)
+    check_rope(q_rope, k_rope, ref, w.kv_dtype)
+    check_out(name, w.describe(), out, lse, ref["out"], ref["lse"], w.kv_dtype)
+
+
+def test_step_parity_serving_scale_sampled():
+    """Full serving shape on the GPU; the oracle recomputes sampled trees."""
+    w = W.WORKLOADS[W.SERVING]
+    inp = W.make_inputs(w)
+    out, lse, q_rope, k_rope = run_step(inp)
+    sample = [0, 13, w.B - 1]
+    ref = O.verify_step(inp["q_lat"], inp["q_rope"], inp["c_kv"], inp["k_rope"], inp["parent"], w.prefix_len,
+                        w.theta, w.sm_scale, w.kv_dtype, batches=sample)
+    check_rope(q_rope, k_rope, ref, w.kv_dtype)
+    check_out(w.name + f" sampled b={sample}", w.describe(), out, lse, ref["out"], ref["lse"], w.kv_dtype,
+              rows=sample)
+
+
+# ---------------------------------------------------------------------------
+# Attention alone on oracle-rotated inputs, edge and ragged shapes
+# ---------------------------------------------------------------------------
+EDGE = [
+    # B, H, q_len, prefix, d_c, d_r, dtype, tree
+    (1, 1, 1, 0, 64, 32, "f32", "chain"),      # single node, no prefix
+    (2, 3, 1, 100, 128, 32, "f32", "chain"),   # autoregressive decode (budget 0)
+    (1, 2, 64, 37, 64, 32, "f32", "rrt"),      # largest tree
+    (1, 2, 64, 0, 64, 64, "f32", "chain"),     # largest chain, no prefix (causal prefill)
+    (1, 1, 1, 5000, 512, 64, "f32", "chain"),  # long prefix, one row: split-kv + merge
+    (2, 4, 9, 3001, 512, 64, "f32", "branch4"),
+    (3, 5, 7, 1000, 256, 64, "bf16", "rrt"),   # ragged everything
+    (2, 4, 64, 200, 512, 64, "bf16", "wide"),
+    (1, 16, 33, 300, 512, 64, "bf16", "branch4"),
+    (2, 64, 33, 700, 512, 64, "bf16", "branch4"),
+    (1, 7, 13, 129, 512, 32, "f32", "rrt"),
+]
+
+
+def _edge_inputs(B, H, q, P, d_c, d_r, dt, tree, seed):
+    rng = np.random.default_rng(seed)
+    kv = P + q
+    scale = 0.5 if dt == "bf16" else 1.0
+    q_lat = (rng.standard_normal((B, q, H, d_c), dtype=np.float32) * scale).astype(np.float32)
+    q_rope = (rng.standard_normal((B, q, H, d_r), dtype=np.float32) * scale).astype(np.float32)
+    c_kv = (rng.standard_normal((B, kv, d_c), dtype=np.float32) * scale).astype(np.float32)
+    k_rope = (rng.standard_normal((B, kv, d_r), dtype=np.float32) * scale).astype(np.float32)
+    if dt == "bf16":
+        c_kv, k_rope = W.f32_to_bf16_bits(c_kv), W.f32_to_bf16_bits(k_rope)
+    parent = np.stack([W.TREES[tree](q, rng) for _ in range(B)]).astype(np.int32)
+    return q_lat, q_rope, c_kv, k_rope, parent
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}H{c[1]}q{c[2]}P{c[3]}dc{c[4]}dr{c[5]}{c[6]}{c[7]}" for c in EDGE])
+def test_attention_edge_shapes(case):
+    B, H, q, P, d_c, d_r, dt, tree = case
+    q_lat, q_rope, c_kv, k_rope, parent = _edge_inputs(*case, seed=zlib.crc32(str(case).encode()))
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, dt),
+                                     O.as_f64(k_rope, dt), parent, P, sm)
+    out, lse = tv.verify_attn(cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, dt), cuda_cache(k_rope, dt),
+                              torch.from_numpy(parent).cuda(), P, sm, return_lse=True)
+    torch.cuda.synchronize()
+    check_out("edge", str(case), out, lse, ref_out, ref_lse, dt)
+
+
+# ---------------------------------------------------------------------------
+# RoPE and positions alone
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d_r", [32, 64, 128])
+def test_rope_bitwise(dt, d_r):
+    rng = np.random.default_rng(d_r)
+    n_seq, n_tok, n_head = 3, 50, 4
+    x = rng.standard_normal((n_seq, n_tok, n_head, d_r), dtype=np.float32)
+    if dt == "bf16":
+        x = W.f32_to_bf16_bits(x)
+    pos = rng.integers(0, 9000, size=(n_seq, n_tok)).astype(np.int32)
+    ref = O.rope_neox_stored(O.as_f64(x, dt), pos[:, :, None], 10000.0, dt)
+    xt = cuda_cache(x, dt)
+    tv.rope_neox(xt, torch.from_numpy(pos).cuda(), 10000.0)
+    torch.cuda.synchronize()
+    if dt == "bf16":
+        u = ulp_diff_bf16(cache_numpy(xt, dt), O.f64_to_bf16_bits(ref))
+    else:
+        u = ulp_diff_f32(xt.cpu().numpy(), ref.astype(np.float32))
+    assert u.max() <= 1 and (u > 0).mean() <= 1e-3, (u.max(), (u > 0).mean())
+
+
+def test_rope_strided_view_and_default_positions():
+    """Rotating a slice of a cache (strided rows) with pos=None uses the row index."""
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((2, 40, 64), dtype=np.float32)
+    kt = cuda_f32(k)
+    tv.rope_neox(kt[:, 3:30, :], None, 10000.0)
+    torch.cuda.synchronize()
+    got = kt.cpu().numpy()
+    ref = O.rope_neox_stored(k[:, 3:30].astype(np.float64), np.arange(27)[None, :], 10000.0, "f32")
+    assert np.array_equal(got[:, :3], k[:, :3]) and np.array_equal(got[:, 30:], k[:, 30:])
+    u = ulp_diff_f32(got[:, 3:30], ref.astype(np.float32))
+    assert u.max() <= 1
+
+
+def test_tree_positions_exact():
+    rng = np.random.default_rng(6)
+    for q in (1, 2, 9, 33, 64):
+        parent = np.stack([W.tree_rrt(q, rng), W.tree_chain(q), W.tree_branch(q, rng)]).astype(np.int32)
+        got = tv.tree_positions(torch.from_numpy(parent).cuda(), 8192).cpu().numpy()
+        assert np.array_equal(got, O.node_positions(parent, 8192))
+
+
+# ---------------------------------------------------------------------------
+# Mask invariants on the GPU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_non_ancestors_bitwise(dt):
+    B, H, q, P, d_c, d_r = 2, 8, 17, 300, 512, 64
+    q_lat, q_rope, c_kv, k_rope, parent = _edge_inputs(B, H, q, P, d_c, d_r, dt, "rrt", seed=7)
+    args = lambda ck, kr: (cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(ck, dt), cuda_cache(kr, dt),
+                           torch.from_numpy(parent).cuda(), P, 0.04)
+    base = tv.verify_attn(*args(c_kv, k_rope)).cpu().numpy()
+    big = W.f32_to_bf16_bits(np.full(d_c, 3.0e4, np.float32)) if dt == "bf16" else np.float32(3.0e4)
+    for b in range(B):
+        for i in (0, q // 2, q - 1):
+            anc = set(O.ancestors_of(parent[b], i))
+            ck, kr = c_kv.copy(), k_rope.copy()
+            for m in range(q):
+                if m not in anc:
+                    ck[b, P + m] = big
+                    kr[b, P + m] = big if dt == "f32" else big[:d_r]
+            got = tv.verify_attn(*args(ck, kr)).cpu().numpy()
+            assert np.array_equal(got[b, i], base[b, i]), (b, i)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_constant_latent_and_root_copy(dt):
+    B, H, q, P, d_c, d_r = 2, 4, 9, 0, 512, 64
+    q_lat, q_rope, c_kv, k_rope, parent = _edge_inputs(B, H, q, P, d_c, d_r, dt, "rrt", seed=8)
+    pt = torch.from_numpy(parent).cuda()
+    # Root with no prefix sees only its own row: the output is that row exactly.
+    out = tv.verify_attn(cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, dt), cuda_cache(k_rope, dt), pt, P,
+                         0.04).cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(out[b, 0], np.broadcast_to(O.as_f64(c_kv, dt)[b, 0].astype(np.float32), (H, d_c)))
+    # A constant latent of ones gives ones (softmax rows sum to 1).
+    ones = np.ones_like(O.as_f64(c_kv, dt), dtype=np.float32)
+    ones_c = W.f32_to_bf16_bits(ones) if dt == "bf16" else ones
+    out1 = tv.verify_attn(cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(ones_c, dt), cuda_cache(k_rope, dt), pt,
+                          P, 0.04).cpu().numpy()
+    assert np.max(np.abs(out1 - 1.0)) <= 4 * 2.0 ** -23

@@ -1,0 +1,153 @@
+// NeoX RoPE with float64 angles, and tree-node positions.
+//
+// [RoPE page = "Precision as Correctness: The Float64 RoPE Decision in a Custom
+//  CUDA Inference Engine", sections "The Message", "The Float64 Decision" and
+//  "What Input Knowledge Is Required" item 1]: the rope slice is split into two
+// halves, pair k = (x[k], x[k + d/2]) turns by pos * inv_freq[k], and the angle,
+// cos, sin and the rotation are evaluated in float64 with a single rounding
+// back to the storage type at the end.
+//
+// The work is element-wise and memory-bound (the same page, "Assumptions and
+// Potential Pitfalls" item 2): each thread owns one pair of one row, so a wave
+// touches 64 consecutive elements of each half of a row.  MI355X runs FP64 at
+// half the FP32 rate, so the float64 sin/cos cost is hidden behind HBM traffic.
+#include "tv_kernels.h"
+
+namespace tv {
+
+// The rotation itself.  Contraction into FMA is disabled so that each product
+// and each sum is rounded in float64 exactly as written.
+__device__ __forceinline__ void rotate_pair_f64(double x1, double x2, double ang, double& y1, double& y2) {
+#pragma clang fp contract(off)
+  double s, c;
+  sincos(ang, &s, &c);
+  y1 = x1 * c - x2 * s;
+  y2 = x2 * c + x1 * s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_neox_kernel(typename T::storage* __restrict__ x,
+                                                        const int32_t* __restrict__ pos, int n_tok, int n_head,
+                                                        int half, int64_t seq_stride, int64_t tok_stride,
+                                                        int64_t pos_seq_stride, int64_t total, RopeFreq f) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int k = static_cast<int>(idx % half);
+  int64_t rest = idx / half;
+  const int h = static_cast<int>(rest % n_head);
+  rest /= n_head;
+  const int t = static_cast<int>(rest % n_tok);
+  const int64_t s = rest / n_tok;
+  const int p = pos ? pos[s * pos_seq_stride + t] : t;
+  typename T::storage* row = x + s * seq_stride + static_cast<int64_t>(t) * tok_stride + static_cast<int64_t>(h) * 2 * half;
+  const double x1 = load_f64<T>(row + k);
+  const double x2 = load_f64<T>(row + k + half);
+  double y1, y2;
+  rotate_pair_f64(x1, x2, static_cast<double>(p) * f.inv_freq[k], y1, y2);
+  store_from_f64<T>(row + k, y1);
+  store_from_f64<T>(row + k + half, y2);
+}
+
+// Depth of every node of one tree, into LDS: thread i walks i -> parent -> ...
+// -> root.  Parents are clamped (clamp_parent), so every walk strictly
+// descends in node index and ends within q_len steps.
+__device__ __forceinline__ void tree_depths_lds(const int32_t* __restrict__ parent_b, int q_len, int* s_parent,
+                                                int* s_depth) {
+  for (int i = threadIdx.x; i < q_len; i += blockDim.x) s_parent[i] = clamp_parent(parent_b[i], i);
+  __syncthreads();
+  for (int i = threadIdx.x; i < q_len; i += blockDim.x) {
+    int d = 0;
+    for (int n = s_parent[i]; n >= 0; n = s_parent[n]) ++d;
+    s_depth[i] = d;
+  }
+  __syncthreads();
+}
+
+// One block per tree.
+__global__ __launch_bounds__(64) void tree_positions_kernel(const int32_t* __restrict__ parent, int q_len,
+                                                            int prefix_len, int32_t* __restrict__ pos) {
+  __shared__ int s_parent[kMaxQ];
+  __shared__ int s_depth[kMaxQ];
+  const int b = blockIdx.x;
+  tree_depths_lds(parent + static_cast<int64_t>(b) * q_len, q_len, s_parent, s_depth);
+  for (int i = threadIdx.x; i < q_len; i += blockDim.x) pos[static_cast<int64_t>(b) * q_len + i] = prefix_len + s_depth[i];
+}
+
+// The step's rotation: for tree b (blockIdx.y), every query row q_rope[b,i,h,:]
+// and the tree's own key row k_rope[b, prefix+i, :] turn at prefix + depth(i).
+// blockIdx.x strides over the (node, head-or-key, pair) triples of the tree.
+template <typename KV>
+__global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_rope,
+                                                        typename KV::storage* __restrict__ k_rope,
+                                                        const int32_t* __restrict__ parent, int q_len, int H,
+                                                        int half, int prefix_len, int kv_len, RopeFreq f) {
+  __shared__ int s_parent[kMaxQ];
+  __shared__ int s_depth[kMaxQ];
+  const int b = blockIdx.y;
+  tree_depths_lds(parent + static_cast<int64_t>(b) * q_len, q_len, s_parent, s_depth);
+  const int per_node = (H + 1) * half;
+  const int total = q_len * per_node;
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
+    const int i = idx / per_node;
+    const int rem = idx - i * per_node;
+    const int h = rem / half;
+    const int k = rem - h * half;
+    const double ang = static_cast<double>(prefix_len + s_depth[i]) * f.inv_freq[k];
+    double y1, y2;
+    if (h < H) {
+      float* row = q_rope + ((static_cast<int64_t>(b) * q_len + i) * H + h) * 2 * half;
+      rotate_pair_f64(static_cast<double>(row[k]), static_cast<double>(row[k + half]), ang, y1, y2);
+      row[k] = static_cast<float>(y1);
+      row[k + half] = static_cast<float>(y2);
+    } else {
+      typename KV::storage* row = k_rope + (static_cast<int64_t>(b) * kv_len + prefix_len + i) * 2 * half;
+      rotate_pair_f64(load_f64<KV>(row + k), load_f64<KV>(row + k + half), ang, y1, y2);
+      store_from_f64<KV>(row + k, y1);
+      store_from_f64<KV>(row + k + half, y2);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_rope_neox(void* x, bool bf16, const int32_t* pos, int n_seq, int n_tok, int n_head, int d_r,
+                            int64_t seq_stride, int64_t tok_stride, int64_t pos_seq_stride, const RopeFreq& f,
+                            hipStream_t stream) {
+  const int half = d_r / 2;
+  const int64_t total = static_cast<int64_t>(n_seq) * n_tok * n_head * half;
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (bf16)
+    rope_neox_kernel<BF16><<<dim3(static_cast<unsigned>(blocks)), threads, 0, stream>>>(
+        static_cast<uint16_t*>(x), pos, n_tok, n_head, half, seq_stride, tok_stride, pos_seq_stride, total, f);
+  else
+    rope_neox_kernel<F32><<<dim3(static_cast<unsigned>(blocks)), threads, 0, stream>>>(
+        static_cast<float*>(x), pos, n_tok, n_head, half, seq_stride, tok_stride, pos_seq_stride, total, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_positions(const int32_t* parent, int B, int q_len, int prefix_len, int32_t* pos,
+                                 hipStream_t stream) {
+  tree_positions_kernel<<<dim3(B), 64, 0, stream>>>(parent, q_len, prefix_len, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_rope(float* q_rope, void* k_rope, bool bf16, const int32_t* parent, int B, int q_len, int H,
+                            int d_r, int prefix_len, const RopeFreq& f, hipStream_t stream) {
+  const int half = d_r / 2;
+  const int total = q_len * (H + 1) * half;
+  const int threads = 256;
+  const int bx = (total + threads - 1) / threads;
+  const int kv_len = prefix_len + q_len;
+  if (bf16)
+    tree_rope_kernel<BF16><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, q_len,
+                                                                 H, half, prefix_len, kv_len, f);
+  else
+    tree_rope_kernel<F32><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, q_len, H,
+                                                                half, prefix_len, kv_len, f);
+  return hipGetLastError();
+}
+
+}  // namespace tv

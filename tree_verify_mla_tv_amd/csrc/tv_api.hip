@@ -1,0 +1,178 @@
+// The C ABI of libtv.so (declared in include/tv.h): argument checks, launch
+// planning and kernel dispatch.  Nothing here allocates or synchronises.
+#include <math.h>
+
+#include "../../include/tv.h"
+#include "tv_kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_attn(int32_t d_c, int32_t d_r, tv_dtype_t dt) {
+  const bool dc_ok = d_c == 64 || d_c == 128 || d_c == 256 || d_c == 512;
+  const bool dr_ok = d_r == 32 || d_r == 64;
+  const bool dt_ok = dt == TV_F32 || dt == TV_BF16;
+  return dc_ok && dr_ok && dt_ok;
+}
+
+tv::RopeFreq make_freq(int32_t d_r, double theta) {
+  tv::RopeFreq f{};
+  const int half = d_r / 2;
+  for (int k = 0; k < half; ++k) f.inv_freq[k] = 1.0 / pow(theta, (2.0 * k) / static_cast<double>(d_r));
+  return f;
+}
+
+// Shape checks shared by tv_verify_attn and tv_verify_step.
+tv_status_t check_attn_shape(int32_t prefix_len, int32_t B, int32_t H, int32_t q_len, int32_t d_c, int32_t d_r,
+                             tv_dtype_t kv_dtype) {
+  if (B < 1 || H < 1 || q_len < 1 || prefix_len < 0) return TV_ERR_INVALID;
+  if (d_c < 1 || d_r < 1 || (d_r & 1)) return TV_ERR_INVALID;
+  if (kv_dtype != TV_F32 && kv_dtype != TV_BF16) return TV_ERR_INVALID;
+  if (q_len > TV_MAX_Q_LEN) return TV_ERR_UNSUPPORTED;
+  if (prefix_len > INT32_MAX - TV_MAX_Q_LEN) return TV_ERR_INVALID;
+  if (static_cast<int64_t>(q_len) * H > (1 << 24)) return TV_ERR_UNSUPPORTED;
+  if (!supported_attn(d_c, d_r, kv_dtype)) return TV_ERR_UNSUPPORTED;
+  return TV_OK;
+}
+
+tv::AttnShape make_shape(int32_t prefix_len, int32_t B, int32_t H, int32_t q_len, int32_t d_c, int32_t d_r,
+                         tv_dtype_t kv_dtype) {
+  return tv::AttnShape{B, H, q_len, prefix_len, prefix_len + q_len, d_c, d_r, kv_dtype == TV_BF16};
+}
+
+tv_status_t run_attention(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                          const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                          int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const tv::AttnShape s = make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype);
+  const tv::AttnPlan plan = tv::plan_attention(s);
+  if (workspace_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && (workspace == nullptr || !aligned16(workspace))))
+    return TV_ERR_INVALID;
+  tv::AttnArgs a{};
+  a.q_lat = q_lat;
+  a.q_rope = q_rope;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.parent = parent;
+  a.out = out;
+  a.lse = lse;
+  if (plan.ws_bytes > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
+    a.ws_m = reinterpret_cast<float*>(ws + plan.ws_m_off);
+    a.ws_l = reinterpret_cast<float*>(ws + plan.ws_l_off);
+  }
+  a.B = B;
+  a.H = H;
+  a.q_len = q_len;
+  a.prefix_len = prefix_len;
+  a.kv_len = s.kv_len;
+  a.R = q_len * H;
+  a.n_rb = plan.n_rb;
+  a.n_split = plan.n_split;
+  a.chunk = plan.chunk;
+  a.sm_scale = sm_scale;
+  return tv::launch_attention(s, plan, a, stream) == hipSuccess ? TV_OK : TV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tv_status_str(tv_status_t s) {
+  switch (s) {
+    case TV_OK: return "TV_OK";
+    case TV_ERR_INVALID: return "TV_ERR_INVALID: invalid argument";
+    case TV_ERR_UNSUPPORTED: return "TV_ERR_UNSUPPORTED: shape or dtype not supported";
+    case TV_ERR_LAUNCH: return "TV_ERR_LAUNCH: kernel launch failed";
+  }
+  return "TV_ERR_UNKNOWN";
+}
+
+tv_status_t tv_tree_positions(const int32_t* parent, int32_t B, int32_t q_len, int32_t prefix_len, int32_t* pos,
+                              hipStream_t stream) {
+  if (!parent || !pos || B < 1 || q_len < 1 || prefix_len < 0) return TV_ERR_INVALID;
+  if (q_len > TV_MAX_Q_LEN) return TV_ERR_UNSUPPORTED;
+  if (prefix_len > INT32_MAX - TV_MAX_Q_LEN) return TV_ERR_INVALID;
+  return tv::launch_tree_positions(parent, B, q_len, prefix_len, pos, stream) == hipSuccess ? TV_OK
+                                                                                            : TV_ERR_LAUNCH;
+}
+
+tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t n_seq, int32_t n_tok,
+                         int32_t n_head, int32_t d_r, int64_t seq_stride, int64_t tok_stride,
+                         int64_t pos_seq_stride, double theta, hipStream_t stream) {
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID;
+  if (n_seq < 0 || n_tok < 0 || n_head < 1 || d_r < 2 || (d_r & 1)) return TV_ERR_INVALID;
+  if (d_r > 2 * tv::kMaxHalf) return TV_ERR_UNSUPPORTED;
+  if (!(theta > 0.0) || !isfinite(theta)) return TV_ERR_INVALID;
+  if (n_seq == 0 || n_tok == 0) return TV_OK;
+  if (!x || seq_stride < 0 || tok_stride < 0 || pos_seq_stride < 0) return TV_ERR_INVALID;
+  if (!aligned16(x) || (pos && (reinterpret_cast<uintptr_t>(pos) & 3u))) return TV_ERR_INVALID;
+  const tv::RopeFreq f = make_freq(d_r, theta);
+  return tv::launch_rope_neox(x, dtype == TV_BF16, pos, n_seq, n_tok, n_head, d_r, seq_stride, tok_stride,
+                              pos_seq_stride, f, stream) == hipSuccess
+             ? TV_OK
+             : TV_ERR_LAUNCH;
+}
+
+size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_t prefix_len, int32_t d_c,
+                                     int32_t d_r, tv_dtype_t kv_dtype) {
+  if (check_attn_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype) != TV_OK) return 0;
+  return tv::plan_attention(make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype)).ws_bytes;
+}
+
+tv_status_t tv_verify_attn(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                           const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                           int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const tv_status_t st = check_attn_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype);
+  if (st != TV_OK) return st;
+  if (!q_lat || !q_rope || !c_kv || !k_rope || !parent || !out) return TV_ERR_INVALID;
+  if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(parent) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return TV_ERR_INVALID;
+  if (!isfinite(sm_scale)) return TV_ERR_INVALID;
+  return run_attention(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, B, H, q_len, d_c, d_r, kv_dtype, sm_scale,
+                       out, lse, workspace, workspace_bytes, stream);
+}
+
+tv_status_t tv_tree_rope(float* q_rope, void* k_rope, tv_dtype_t kv_dtype, const int32_t* parent,
+                         int32_t prefix_len, int32_t B, int32_t H, int32_t q_len, int32_t d_r, double theta,
+                         hipStream_t stream) {
+  if (kv_dtype != TV_F32 && kv_dtype != TV_BF16) return TV_ERR_INVALID;
+  if (B < 1 || H < 1 || q_len < 1 || prefix_len < 0 || d_r < 2 || (d_r & 1)) return TV_ERR_INVALID;
+  if (q_len > TV_MAX_Q_LEN || d_r > 2 * tv::kMaxHalf) return TV_ERR_UNSUPPORTED;
+  if (prefix_len > INT32_MAX - TV_MAX_Q_LEN) return TV_ERR_INVALID;
+  if (static_cast<int64_t>(q_len) * (H + 1) * (d_r / 2) > INT32_MAX) return TV_ERR_UNSUPPORTED;
+  if (!(theta > 0.0) || !isfinite(theta)) return TV_ERR_INVALID;
+  if (!q_rope || !k_rope || !parent) return TV_ERR_INVALID;
+  if (!aligned16(q_rope) || !aligned16(k_rope) || (reinterpret_cast<uintptr_t>(parent) & 3u)) return TV_ERR_INVALID;
+  const tv::RopeFreq f = make_freq(d_r, theta);
+  return tv::launch_tree_rope(q_rope, k_rope, kv_dtype == TV_BF16, parent, B, q_len, H, d_r, prefix_len, f, stream) ==
+                 hipSuccess
+             ? TV_OK
+             : TV_ERR_LAUNCH;
+}
+
+tv_status_t tv_verify_step(const float* q_lat, float* q_rope, const void* c_kv, void* k_rope,
+                           const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                           int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, double theta, float sm_scale,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const tv_status_t st = check_attn_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype);
+  if (st != TV_OK) return st;
+  if (!q_lat || !q_rope || !c_kv || !k_rope || !parent || !out) return TV_ERR_INVALID;
+  if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(parent) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return TV_ERR_INVALID;
+  if (!isfinite(sm_scale) || !(theta > 0.0) || !isfinite(theta)) return TV_ERR_INVALID;
+  const tv::AttnPlan plan = tv::plan_attention(make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype));
+  if (workspace_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && (workspace == nullptr || !aligned16(workspace))))
+    return TV_ERR_INVALID;
+  const tv_status_t rs = tv_tree_rope(q_rope, k_rope, kv_dtype, parent, prefix_len, B, H, q_len, d_r, theta, stream);
+  if (rs != TV_OK) return rs;
+  return run_attention(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, B, H, q_len, d_c, d_r, kv_dtype, sm_scale,
+                       out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

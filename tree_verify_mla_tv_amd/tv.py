@@ -1,0 +1,228 @@
+"""Thin Python binding of libtv.so (ctypes): argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI of include/tv.h;
+PyTorch only provides device memory and the current stream.  If libtv.so is
+missing the calls raise: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtv.so")
+
+TV_OK, TV_ERR_INVALID, TV_ERR_UNSUPPORTED, TV_ERR_LAUNCH = 0, 1, 2, 3
+TV_F32, TV_BF16 = 0, 1
+TV_MAX_Q_LEN = 64
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_f64 = ctypes.c_double
+_sz = ctypes.c_size_t
+
+SIGNATURES = {
+    "tv_status_str": (ctypes.c_char_p, [_i32]),
+    "tv_tree_positions": (_i32, [_p, _i32, _i32, _i32, _p, _p]),
+    "tv_rope_neox": (_i32, [_p, _i32, _p, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _f64, _p]),
+    "tv_verify_attn": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
+                              _sz, _p]),
+    "tv_verify_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "tv_tree_rope": (_i32, [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f64, _p]),
+    "tv_verify_step": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f64, _f32, _p, _p,
+                              _p, _sz, _p]),
+}
+
+
+class TVError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn}: {status_str(code)}")
+        self.code = code
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m tree_verify_mla_tv_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return load().tv_status_str(code).decode()
+
+
+def _check(fn: str, code: int):
+    if code != TV_OK:
+        raise TVError(fn, code)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TV_F32
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    raise TypeError(f"cache dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _cuda_contig(name: str, t: torch.Tensor):
+    _need(t.is_cuda, f"{name} must be a CUDA (HIP) tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def tree_positions(parent: torch.Tensor, prefix_len: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """pos[b, i] = prefix_len + depth(i) for parent arrays [B, q_len] (int32)."""
+    _cuda_contig("parent", parent)
+    _need(parent.dtype == torch.int32 and parent.dim() == 2, "parent must be int32 [B, q_len]")
+    B, q = parent.shape
+    if out is None:
+        out = torch.empty_like(parent)
+    _check("tv_tree_positions", load().tv_tree_positions(_ptr(parent), B, q, prefix_len, _ptr(out), _stream()))
+    return out
+
+
+def rope_neox(x: torch.Tensor, pos: torch.Tensor | None = None, theta: float = 10000.0) -> torch.Tensor:
+    """In-place NeoX RoPE (float64 angles) of x [n_seq, n_tok, (n_head,) d_r].
+
+    The head and feature axes must be dense; the sequence and token axes may be
+    strided (e.g. a slice of a kv cache).  pos: int32 [n_seq, n_tok] (row stride
+    free), or None for position = token index.
+    """
+    _need(x.is_cuda, "x must be a CUDA tensor")
+    if x.dim() == 3:
+        n_seq, n_tok, d_r = x.shape
+        n_head = 1
+    else:
+        _need(x.dim() == 4, "x must be [n_seq, n_tok, n_head, d_r] or [n_seq, n_tok, d_r]")
+        n_seq, n_tok, n_head, d_r = x.shape
+        _need(n_head == 1 or x.stride(2) == d_r, "heads of x must be dense rows")
+    _need(x.stride(-1) == 1, "the feature axis of x must be contiguous")
+    dt = _kv_dtype(x)
+    pos_stride = 0
+    if pos is not None:
+        _need(pos.is_cuda and pos.dtype == torch.int32 and pos.shape == (n_seq, n_tok) and pos.stride(1) == 1,
+              "pos must be CUDA int32 [n_seq, n_tok] with unit token stride")
+        pos_stride = pos.stride(0)
+    _check("tv_rope_neox", load().tv_rope_neox(_ptr(x), dt, _ptr(pos), n_seq, n_tok, n_head, d_r, x.stride(0),
+                                               x.stride(1), pos_stride, float(theta), _stream()))
+    return x
+
+
+def workspace_size(B: int, H: int, q_len: int, prefix_len: int, d_c: int, d_r: int, kv_dtype: int) -> int:
+    return int(load().tv_verify_attn_workspace_size(B, H, q_len, prefix_len, d_c, d_r, kv_dtype))
+
+
+def _attn_shapes(q_lat, q_rope, c_kv, k_rope, parent, prefix_len):
+    for n, t in (("q_lat", q_lat), ("q_rope", q_rope), ("c_kv", c_kv), ("k_rope", k_rope), ("parent", parent)):
+        _cuda_contig(n, t)
+    _need(q_lat.dtype == torch.float32 and q_rope.dtype == torch.float32, "q_lat and q_rope must be float32")
+    _need(parent.dtype == torch.int32, "parent must be int32")
+    _need(c_kv.dtype == k_rope.dtype, "c_kv and k_rope must share a dtype")
+    B, q, H, d_c = q_lat.shape
+    d_r = q_rope.shape[-1]
+    kv = prefix_len + q
+    _need(q_rope.shape == (B, q, H, d_r), f"q_rope must be {(B, q, H, d_r)}")
+    _need(c_kv.shape == (B, kv, d_c), f"c_kv must be {(B, kv, d_c)}")
+    _need(k_rope.shape == (B, kv, d_r), f"k_rope must be {(B, kv, d_r)}")
+    _need(parent.shape == (B, q), f"parent must be {(B, q)}")
+    return B, q, H, d_c, d_r
+
+
+def _outputs(q_lat, out, lse, return_lse, workspace, ws_bytes):
+    B, q, H, d_c = q_lat.shape
+    if out is None:
+        out = torch.empty_like(q_lat)
+    else:
+        _cuda_contig("out", out)
+        _need(out.shape == q_lat.shape and out.dtype == torch.float32, "out must be float32 like q_lat")
+    if lse is None and return_lse:
+        lse = torch.empty((B, q, H), dtype=torch.float32, device=q_lat.device)
+    if lse is not None:
+        _cuda_contig("lse", lse)
+        _need(lse.shape == (B, q, H) and lse.dtype == torch.float32, "lse must be float32 [B, q_len, H]")
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q_lat.device)
+    if workspace is not None:
+        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous CUDA tensor")
+    return out, lse, workspace
+
+
+def verify_attn(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, sm_scale: float | None = None, out=None,
+                lse=None, return_lse: bool = False, workspace=None):
+    """Tree-verify MLA-absorb attention (rope slices already rotated).
+
+    Returns out [B, q_len, H, d_c] float32 (and lse [B, q_len, H] if asked or given).
+    sm_scale defaults to 1/sqrt(d_c + d_r), rounded to fp32.
+    """
+    B, q, H, d_c, d_r = _attn_shapes(q_lat, q_rope, c_kv, k_rope, parent, prefix_len)
+    dt = _kv_dtype(c_kv)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_c + d_r)
+    ws_bytes = workspace_size(B, H, q, prefix_len, d_c, d_r, dt)
+    out, lse_t, workspace = _outputs(q_lat, out, lse, return_lse, workspace, ws_bytes)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tv_verify_attn", load().tv_verify_attn(
+        _ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
+        float(sm_scale), _ptr(out), _ptr(lse_t), _ptr(workspace), ws_n, _stream()))
+    return (out, lse_t) if (return_lse or lse is not None) else out
+
+
+def tree_rope(q_rope, k_rope, parent, prefix_len: int, theta: float = 10000.0):
+    """Rotate q_rope [B,q,H,d_r] and the tree's key rows k_rope[:, prefix_len:, :]
+    in place at prefix_len + depth(node) (one fused launch)."""
+    _cuda_contig("q_rope", q_rope)
+    _cuda_contig("k_rope", k_rope)
+    _cuda_contig("parent", parent)
+    _need(q_rope.dtype == torch.float32 and q_rope.dim() == 4, "q_rope must be float32 [B, q_len, H, d_r]")
+    _need(parent.dtype == torch.int32, "parent must be int32")
+    B, q, H, d_r = q_rope.shape
+    _need(k_rope.shape == (B, prefix_len + q, d_r), f"k_rope must be {(B, prefix_len + q, d_r)}")
+    _need(parent.shape == (B, q), f"parent must be {(B, q)}")
+    _check("tv_tree_rope", load().tv_tree_rope(_ptr(q_rope), _ptr(k_rope), _kv_dtype(k_rope), _ptr(parent),
+                                               prefix_len, B, H, q, d_r, float(theta), _stream()))
+    return q_rope, k_rope
+
+
+def verify_step(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, theta: float = 10000.0,
+                sm_scale: float | None = None, out=None, lse=None, return_lse: bool = False, workspace=None):
+    """The whole step: rotate q_rope and the tree's key rows in place at
+    prefix_len + depth, then tree-verify attention.  Prefix key rows are taken
+    as already rotated."""
+    B, q, H, d_c, d_r = _attn_shapes(q_lat, q_rope, c_kv, k_rope, parent, prefix_len)
+    dt = _kv_dtype(c_kv)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_c + d_r)
+    ws_bytes = workspace_size(B, H, q, prefix_len, d_c, d_r, dt)
+    out, lse_t, workspace = _outputs(q_lat, out, lse, return_lse, workspace, ws_bytes)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tv_verify_step", load().tv_verify_step(
+        _ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
+        float(theta), float(sm_scale), _ptr(out), _ptr(lse_t), _ptr(workspace), ws_n, _stream()))
+    return (out, lse_t) if (return_lse or lse is not None) else out
