@@ -36,8 +36,8 @@ PEAKS_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32_mfma": 157.3, "f32_valu": 15
 # Which kernel the library runs for each cache dtype, the arithmetic it does,
 # and the roofline that bounds it.
 KERNELS = {
-    "bf16": dict(name="attn_valu_kernel", source="tree_verify_mla_tv_amd/csrc/attn_valu.hip", bound="alu",
-                 peak="f32_valu", dtype="f32"),
+    "bf16": dict(name="attn_mfma_bf16_kernel", source="tree_verify_mla_tv_amd/csrc/attn_mfma.hip", bound="mfma",
+                 peak="bf16", dtype="bf16"),
     "f32": dict(name="attn_valu_kernel", source="tree_verify_mla_tv_amd/csrc/attn_valu.hip", bound="alu",
                 peak="f32_valu", dtype="f32"),
 }

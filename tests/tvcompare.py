@@ -46,3 +46,32 @@ def ulp_diff_bf16(a_bits, b_bits) -> np.ndarray:
     ia = np.where(ia & 0x8000, -(ia & 0x7FFF), ia)
     ib = np.where(ib & 0x8000, -(ib & 0x7FFF), ib)
     return np.abs(ia - ib)
+
+
+def rope_mismatch(got, ref, x_raw, dtype: str, max_pos: int):
+    """Compare a stored RoPE result with the oracle's.
+
+    Both sides round the same float64 rotation once; they may differ only where
+    the device's float64 pow/sin/cos differ from the host's in the last bit and
+    the rotated value sits near a rounding boundary, or where the rotation
+    cancels (x1 cos ~ x2 sin) so a float64-level difference is many storage
+    ulps of a tiny result.  A last-bit difference in inv_freq moves the angle
+    by up to pos * 2^-52 rad (relative to inv_freq <= 1), and sin/cos/the
+    rotation add a few 2^-53, so the allowance is
+        |got - ref| <= 1 storage ulp of ref + (|x1| + |x2|) (max_pos + 4) 2^-50.
+    Returns (n_beyond_allowance, fraction_not_identical).
+    """
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    x = np.abs(np.asarray(x_raw, dtype=np.float64))
+    half = x.shape[-1] // 2
+    pair = x[..., :half] + x[..., half:]
+    pair = np.concatenate([pair, pair], axis=-1)
+    if dtype == "bf16":
+        e = np.frexp(np.maximum(np.abs(r), 1e-30))[1]
+        ulp = np.ldexp(1.0, e - 8)
+    else:
+        ulp = np.spacing(np.abs(r).astype(np.float32)).astype(np.float64)
+    d = np.abs(g - r)
+    beyond = int(np.count_nonzero(d > ulp + pair * (max_pos + 4) * 2.0 ** -50))
+    return beyond, float(np.count_nonzero(d) / d.size)

@@ -1,5 +1,5 @@
-// Tree-verify MLA-absorb attention: the FP32 vector-ALU kernel, the split-kv
-// merge, the launch planner and the kernel dispatch.
+// Tree-verify MLA-absorb attention: the FP32 vector-ALU kernel (all supported
+// shapes; the fp32-cache path).
 //
 // [Verify page = "The Precision Imperative: Validating Numerical Accuracy in a
 //  Custom CUDA Attention Kernel", "The Context: What Led to This Moment": masked
@@ -17,9 +17,6 @@
 
 namespace tv {
 
-constexpr int kValuRows = 16;   // query rows per workgroup
-constexpr int kValuKeys = 32;   // kv rows per LDS tile
-constexpr int kValuThreads = 256;
 
 template <typename KV>
 __device__ __forceinline__ float4 load4(const void* base, int64_t elem_off);
@@ -38,19 +35,6 @@ __device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
   acc = fmaf(a.y, b.y, acc);
   acc = fmaf(a.z, b.z, acc);
   return fmaf(a.w, b.w, acc);
-}
-
-// Ancestor bit masks of one tree: bit m of s_anc[i] is set iff node m is node i
-// or one of its ancestors.  Thread i walks its own path (<= q_len steps).
-__device__ __forceinline__ void build_ancestors(const int32_t* __restrict__ parent_b, int q_len, int* s_par,
-                                                unsigned long long* s_anc) {
-  for (int i = threadIdx.x; i < q_len; i += blockDim.x) s_par[i] = clamp_parent(parent_b[i], i);
-  __syncthreads();
-  for (int i = threadIdx.x; i < q_len; i += blockDim.x) {
-    unsigned long long anc = 1ull << i;
-    for (int n = s_par[i]; n >= 0; n = s_par[n]) anc |= 1ull << n;
-    s_anc[i] = anc;
-  }
 }
 
 template <typename KV, int DC, int DR>
@@ -72,13 +56,11 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   __shared__ unsigned long long s_anc[kMaxQ];
 
   const int tid = threadIdx.x;
-  const int split = blockIdx.x % a.n_split;
-  const int rest = blockIdx.x / a.n_split;
-  const int rb = rest % a.n_rb;
-  const int b = rest / a.n_rb;
-  const int r0 = rb * kValuRows;
-  const int k_begin = split * a.chunk;
-  const int k_end = min(a.kv_len, k_begin + a.chunk);
+  const Unit w = decode_unit(a, blockIdx.x);
+  const int b = w.b;
+  const int r0 = w.rb * kValuRows;
+  const int k_begin = w.k_begin;
+  const int k_end = w.k_end;
   const int P = a.prefix_len;
 
   build_ancestors(a.parent + static_cast<int64_t>(b) * a.q_len, a.q_len, s_par, s_anc);
@@ -208,11 +190,11 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float4 v = make_float4(o[i].x * inv, o[i].y * inv, o[i].z * inv, o[i].w * inv);
     const int64_t grow = static_cast<int64_t>(b) * a.R + row;
-    if (a.n_split == 1) {
+    if (w.slot < 0) {
       *reinterpret_cast<float4*>(a.out + grow * DC + col4 * 4) = v;
       if (col4 == 0 && a.lse) a.lse[grow] = m + logf(l);
     } else {
-      const int64_t srow = static_cast<int64_t>(split) * a.B * a.R + grow;
+      const int64_t srow = w.slot * kValuRows + r;
       *reinterpret_cast<float4*>(a.ws_o + srow * DC + col4 * 4) = v;
       if (col4 == 0) {
         a.ws_m[srow] = m;
@@ -222,78 +204,9 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   }
 }
 
-// Combine split partials: w_s = l_s * exp(m_s - max_s m_s), out = sum w_s o_s / sum w_s,
-// lse = max m + log(sum w_s).  One thread per (row, float4 column).
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c) {
-  const int cpt = d_c / 4;
-  const int64_t total = static_cast<int64_t>(a.B) * a.R * cpt;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int64_t grow = idx / cpt;
-  const int col4 = static_cast<int>(idx - grow * cpt);
-  const int64_t stride = static_cast<int64_t>(a.B) * a.R;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.ws_m[s * stride + grow]);
-  float W = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < a.n_split; ++s) {
-    const float l = a.ws_l[s * stride + grow];
-    if (!(l > 0.f)) continue;
-    const float w = l * expf(a.ws_m[s * stride + grow] - M);
-    const float4 v = *reinterpret_cast<const float4*>(a.ws_o + (s * stride + grow) * d_c + col4 * 4);
-    W += w;
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
-  }
-  const float inv = 1.f / W;
-  *reinterpret_cast<float4*>(a.out + grow * d_c + col4 * 4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (col4 == 0 && a.lse) a.lse[grow] = M + logf(W);
-}
-
-// ---------------------------------------------------------------------------
-// Planning and dispatch
-// ---------------------------------------------------------------------------
-namespace {
-constexpr int kNumCU = 256;  // MI355X; fixed so plans depend on shapes only
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-}  // namespace
-
-AttnPlan plan_attention(const AttnShape& s) {
-  AttnPlan p{};
-  p.kernel = AttnKernel::kValu;
-  p.rows_per_block = kValuRows;
-  p.keys_per_tile = kValuKeys;
-  const int R = s.q_len * s.H;
-  p.n_rb = (R + p.rows_per_block - 1) / p.rows_per_block;
-  const long long units = static_cast<long long>(s.B) * p.n_rb;
-  int n_split = 1;
-  if (units < 2 * kNumCU) {
-    const long long want = (2 * kNumCU + units - 1) / units;
-    const int max_split = s.kv_len / 128 > 1 ? s.kv_len / 128 : 1;  // >= 128 kv rows per split
-    n_split = static_cast<int>(want < max_split ? want : max_split);
-  }
-  int chunk = (s.kv_len + n_split - 1) / n_split;
-  chunk = (chunk + p.keys_per_tile - 1) / p.keys_per_tile * p.keys_per_tile;
-  n_split = (s.kv_len + chunk - 1) / chunk;
-  p.n_split = n_split;
-  p.chunk = chunk;
-  p.ws_bytes = 0;
-  if (n_split > 1) {
-    const size_t rows = static_cast<size_t>(n_split) * s.B * R;
-    p.ws_o_off = 0;
-    p.ws_m_off = align256(rows * s.d_c * sizeof(float));
-    p.ws_l_off = p.ws_m_off + align256(rows * sizeof(float));
-    p.ws_bytes = p.ws_l_off + align256(rows * sizeof(float));
-  }
-  return p;
-}
-
 template <typename KV, int DC>
 static hipError_t launch_valu_dr(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(static_cast<long long>(s.B) * plan.n_rb * plan.n_split));
+  const dim3 grid(static_cast<unsigned>(plan.units));
   if (s.d_r == 32)
     attn_valu_kernel<KV, DC, 32><<<grid, kValuThreads, 0, stream>>>(a);
   else
@@ -311,12 +224,8 @@ static hipError_t launch_valu(const AttnShape& s, const AttnPlan& plan, const At
   }
 }
 
-hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  hipError_t e = s.kv_bf16 ? launch_valu<BF16>(s, plan, a, stream) : launch_valu<F32>(s, plan, a, stream);
-  if (e != hipSuccess || plan.n_split == 1) return e;
-  const int64_t total = static_cast<int64_t>(s.B) * a.R * (s.d_c / 4);
-  attn_merge_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), 256, 0, stream>>>(a, s.d_c);
-  return hipGetLastError();
+hipError_t launch_attn_valu(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
+  return s.kv_bf16 ? launch_valu<BF16>(s, plan, a, stream) : launch_valu<F32>(s, plan, a, stream);
 }
 
 }  // namespace tv

@@ -69,9 +69,13 @@ tv_status_t run_attention(const float* q_lat, const float* q_rope, const void* c
   a.prefix_len = prefix_len;
   a.kv_len = s.kv_len;
   a.R = q_len * H;
+  a.rows_per_block = plan.rows_per_block;
   a.n_rb = plan.n_rb;
-  a.n_split = plan.n_split;
-  a.chunk = plan.chunk;
+  a.full_rb = plan.full_rb;
+  a.split_full = plan.split_full;
+  a.chunk_full = plan.chunk_full;
+  a.split_tail = plan.split_tail;
+  a.chunk_tail = plan.chunk_tail;
   a.sm_scale = sm_scale;
   return tv::launch_attention(s, plan, a, stream) == hipSuccess ? TV_OK : TV_ERR_LAUNCH;
 }

@@ -29,18 +29,39 @@ hipError_t launch_tree_rope(float* q_rope, void* k_rope, bool bf16, const int32_
 // ---------------------------------------------------------------------------
 // Attention
 // ---------------------------------------------------------------------------
-enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1, kMfmaF32 = 2 };
+enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1 };
 
-// How one tv_verify_attn call is cut into workgroups.  A pure function of the
-// shapes (never of the device), so the workspace size can be asked for ahead.
+// Workgroup geometry of the two kernel families.
+constexpr int kValuRows = 16;     // query rows per workgroup
+constexpr int kValuKeys = 32;     // kv rows per LDS tile
+constexpr int kValuThreads = 256;
+constexpr int kMfmaRows = 128;    // 4 waves x 32 query rows
+constexpr int kMfmaKeys = 32;
+constexpr int kMfmaThreads = 256;
+
+// How one tv_verify_attn call is cut into workgroups ("units").  A pure
+// function of the shapes (never of the device), so the workspace size can be
+// asked for ahead.
+//
+// The R = q_len * H query rows of a tree are cut into row blocks of
+// rows_per_block; every row block but possibly the last is full.  Full blocks
+// are cut into split_full kv ranges of chunk_full rows, the partial last block
+// into split_tail ranges of chunk_tail rows (a short last round of the grid is
+// then filled by short units).  Units of full blocks come first in launch
+// order.  A row block cut into more than one range writes partial results to
+// the workspace ("slots"), combined afterwards by the merge pass.
 struct AttnPlan {
   AttnKernel kernel;
-  int rows_per_block;  // query rows (node, head) per workgroup
-  int keys_per_tile;   // kv rows staged per LDS tile
-  int n_rb;            // row blocks per batch entry
-  int n_split;         // kv splits (1 = no merge pass)
-  int chunk;           // kv rows per split (multiple of keys_per_tile)
-  size_t ws_bytes;     // workspace for split partials
+  int rows_per_block;
+  int keys_per_tile;
+  int n_rb;        // row blocks per tree
+  int full_rb;     // full row blocks per tree (n_rb or n_rb - 1)
+  int split_full, chunk_full;
+  int split_tail, chunk_tail;  // meaningful when full_rb < n_rb
+  long long units;
+  long long n_slots;           // partial-result slots in the workspace
+  long long merge_blocks;      // row blocks that need merging
+  size_t ws_bytes;
   size_t ws_o_off, ws_m_off, ws_l_off;
 };
 
@@ -59,13 +80,65 @@ struct AttnArgs {
   const int32_t* parent;
   float* out;
   float* lse;
-  float* ws_o;  // [n_split][B][R][d_c]
-  float* ws_m;  // [n_split][B][R]
-  float* ws_l;  // [n_split][B][R]
-  int B, H, q_len, prefix_len, kv_len, R, n_rb, n_split, chunk;
+  float* ws_o;  // [n_slots][rows_per_block][d_c]  (normalised partial outputs)
+  float* ws_m;  // [n_slots][rows_per_block]       (row max, natural-log units)
+  float* ws_l;  // [n_slots][rows_per_block]       (sum of exp(s - m))
+  int B, H, q_len, prefix_len, kv_len, R;
+  int rows_per_block, n_rb, full_rb, split_full, chunk_full, split_tail, chunk_tail;
   float sm_scale;
 };
 
+// The work of one unit (one workgroup).
+struct Unit {
+  int b, rb, split;
+  int k_begin, k_end;
+  long long slot;  // partial-result slot, or -1 when the row block is not split
+};
+
+__device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long long u) {
+  Unit w;
+  const long long units_full = static_cast<long long>(a.B) * a.full_rb * a.split_full;
+  int chunk;
+  if (u < units_full) {
+    w.split = static_cast<int>(u % a.split_full);
+    const long long t = u / a.split_full;
+    w.rb = static_cast<int>(t % a.full_rb);
+    w.b = static_cast<int>(t / a.full_rb);
+    chunk = a.chunk_full;
+    w.slot = a.split_full > 1 ? (static_cast<long long>(w.b) * a.full_rb + w.rb) * a.split_full + w.split : -1;
+  } else {
+    const long long u2 = u - units_full;
+    w.split = static_cast<int>(u2 % a.split_tail);
+    w.b = static_cast<int>(u2 / a.split_tail);
+    w.rb = a.n_rb - 1;
+    chunk = a.chunk_tail;
+    const long long base = a.split_full > 1 ? units_full : 0;
+    w.slot = a.split_tail > 1 ? base + static_cast<long long>(w.b) * a.split_tail + w.split : -1;
+  }
+  w.k_begin = w.split * chunk;
+  w.k_end = min(a.kv_len, w.k_begin + chunk);
+  return w;
+}
+
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+
+// Kernel launchers (one per kernel family).
+hipError_t launch_attn_valu(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_mfma_bf16(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+
+// Ancestor bit masks of one tree: bit m of s_anc[i] is set iff node m is node i
+// or one of its ancestors.  Thread i walks its own path (<= q_len steps).
+// Ends with a barrier.
+__device__ __forceinline__ void build_ancestors(const int32_t* __restrict__ parent_b, int q_len, int* s_par,
+                                                unsigned long long* s_anc) {
+  for (int i = threadIdx.x; i < q_len; i += blockDim.x) s_par[i] = clamp_parent(parent_b[i], i);
+  __syncthreads();
+  for (int i = threadIdx.x; i < q_len; i += blockDim.x) {
+    unsigned long long anc = 1ull << i;
+    for (int n = s_par[i]; n >= 0; n = s_par[n]) anc |= 1ull << n;
+    s_anc[i] = anc;
+  }
+  __syncthreads();
+}
 
 }  // namespace tv
