@@ -30,10 +30,12 @@
 //     ran out of headroom, so nothing overflows for any finite input.
 // Scores of a tile that holds tree rows are masked by the ancestor bit mask.
 #include "tv_kernels.h"
+#include "attn_mfma_asm.h"
 
 namespace tv {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(8))) short i16x8_t;
@@ -42,11 +44,12 @@ namespace mf {
 constexpr int DC = 512, DR = 64, D = DC + DR;
 constexpr int KSTEPS = D / 16;                      // 36 k-steps of the score product
 constexpr int KSTEPS_LAT = DC / 16;                 // 32 of them in the latent part
-constexpr int kPadBytes = 32;                       // gap between latent rows in LDS
-constexpr int kLatRowBytes = DC * 2 + kPadBytes;    // 1056
-constexpr int kLatBytes = kMfmaKeys * kLatRowBytes; // 33792
+constexpr int kPadBytes = 16;                       // gap between latent rows in LDS
+constexpr int kLatRowBytes = DC * 2 + kPadBytes;    // 1040
+constexpr int kLatBytes = kMfmaKeys * kLatRowBytes; // 33280
 constexpr int kRopeBytes = kMfmaKeys * DR * 2;      // 4096
-constexpr int kBufBytes = kLatBytes + kRopeBytes;   // 37888
+constexpr int kBufBytes = kLatBytes + kRopeBytes;   // 37376
+constexpr int kVtBytes = DC * 64;                   // 32768: V^T tile, 512 rows of 32 keys
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kHeadroom = 64.0f;                  // log2 units above m_ref before a re-sweep
@@ -54,12 +57,21 @@ constexpr float kHeadroom = 64.0f;                  // log2 units above m_ref be
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr_t;
 
-__shared__ __align__(16) unsigned char g_kv_buf0[mf::kBufBytes];
-__shared__ __align__(16) unsigned char g_kv_buf1[mf::kBufBytes];
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
+}
 
-// Copy kv rows [kt, kt + 32) of one tree into an LDS tile buffer.  Rows past
-// k_end repeat row k_end - 1 (finite data; their scores are masked).
+// Two kv tiles (row-major, as in HBM) and two transposed latent tiles.
+__shared__ __align__(16) unsigned char g_k0[mf::kBufBytes];
+__shared__ __align__(16) unsigned char g_k1[mf::kBufBytes];
+__shared__ __align__(16) unsigned char g_vt0[mf::kVtBytes];
+__shared__ __align__(16) unsigned char g_vt1[mf::kVtBytes];
+
+// Copy kv rows [kt, kt + 32) of one tree into a row-major tile buffer.  Rows
+// past k_end repeat row k_end - 1 (finite data; their scores are masked).
 //   latent rows:  row k at buf + k * kLatRowBytes, 64 chunks of 16 B; wave w
 //                 copies rows 8w .. 8w+7, one wave-wide 1 KB copy per row.
 //   rope rows:    wave w copies keys 8w .. 8w+7 into buf + kLatBytes + 1024 w,
@@ -81,7 +93,36 @@ __device__ __forceinline__ void stage_tile(unsigned char* buf, const uint16_t* _
   __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src), (lds_ptr_t)(buf + mf::kLatBytes + wave * 1024), 16, 0, 0);
 }
 
-// Everything one wave does with one staged tile.
+// Transposed latent tile V^T: 512 rows d of 4 chunks of 16 B.  Chunk 2h + g of
+// row d holds the 8 keys 16 h + {4 g .. 4 g + 3, 8 + 4 g .. 8 + 4 g + 3} at d,
+// i.e. exactly the A operand lane (d % 32) + 32 g needs for the value MFMA of
+// key half h.  Chunks are XOR-swizzled by (d >> 2) & 3 so the 16 lanes of a
+// 128-bit access hit 16 different bank groups.
+__device__ __forceinline__ int vt_offset(int d, int chunk) { return d * 64 + 16 * (chunk ^ ((d >> 2) & 3)); }
+
+// One wave's quarter of the transpose of a row-major tile (d-blocks 4w..4w+3)
+// into V^T, through ds_read_b64_tr_b16: in each 16-lane group, lane j points at
+// 4 consecutive d of key row kb + j/4 and receives the 4 keys kb .. kb+3 of
+// d = d0 + j.
+__device__ __forceinline__ void transpose_quarter(const unsigned char* kbuf, unsigned char* vt, int lane, int wave) {
+  const int g2 = lane >> 5;
+  const int grp = lane >> 4;
+  const int j = lane & 15;
+  const int d0 = 16 * (grp & 1) + 4 * (j & 3);
+  const unsigned char* vbase = kbuf + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + d0 * 2;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int db = 4 * wave + (u >> 1);
+    const int h = u & 1;
+    const unsigned char* va = vbase + (16 * h) * mf::kLatRowBytes + db * 64;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(va));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(va + 8 * mf::kLatRowBytes));
+    const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    *reinterpret_cast<i16x8_t*>(vt + vt_offset(32 * db + (lane & 31), 2 * h + g2)) = v;
+  }
+}
+
+// Everything one wave keeps across tiles.
 struct WaveState {
   f32x16_t o[16];   // O^T blocks: o[db][i] = out[row][32 db + 8 (i/4) + 4 g2 + i%4]
   float m_ref;      // reference max (log2 units) the exponentials are taken against
@@ -90,33 +131,36 @@ struct WaveState {
   bool over;        // a score exceeded m_ref + kHeadroom
 };
 
-__device__ __forceinline__ void tile_compute(const unsigned char* buf, const bf16x8_t* qf,
-                                             const unsigned char* qrope, WaveState& st, int lane, int kt, int k_end,
-                                             int P, unsigned long long anc) {
+// S^T = K Q^T for one tile, mask, and the tile's softmax weights (bf16).
+__device__ __forceinline__ void qk_softmax(const unsigned char* buf, const bf16x8_t* qf, const unsigned char* qrope,
+                                           WaveState& st, int lane, int kt, int k_end, int P,
+                                           unsigned long long anc, bf16x8_t& p0, bf16x8_t& p1) {
   const int g2 = lane >> 5;
   const int key_l = lane & 31;
-  // ---- S^T = K Q^T: 36 MFMAs 32x32x16, one accumulator chain.  The latent
-  // part of Q is in registers (qf), the rope part in LDS (qrope, chunk-major).
-  f32x16_t sacc = {};
-  const unsigned char* lat = buf + key_l * mf::kLatRowBytes + g2 * 16;
-#pragma unroll
-  for (int ks = 0; ks < mf::KSTEPS_LAT; ++ks) {
-    const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(lat + ks * 32);
-    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc, 0, 0, 0);
-  }
-  const unsigned char* rope = buf + mf::kLatBytes + (key_l >> 3) * 1024 + (key_l & 7) * 16;
-#pragma unroll
-  for (int ks = mf::KSTEPS_LAT; ks < mf::KSTEPS; ++ks) {
-    const int c = g2 + 2 * (ks - mf::KSTEPS_LAT);
-    const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(rope + c * 128);
-    const bf16x8_t q0 = *reinterpret_cast<const bf16x8_t*>(qrope + c * (kMfmaRows * 16));
-    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, q0, sacc, 0, 0, 0);
-  }
+  // 36 MFMAs 32x32x16 in one accumulator chain (TV_QK_ASM, generated): the
+  // latent part of Q is in registers (qf), the rope part in LDS (qrope,
+  // chunk-major); every K fragment is read 4 MFMAs ahead of its use.
+  const uint32_t lat = lds_addr(buf + key_l * mf::kLatRowBytes + g2 * 16);
+  const uint32_t rope = lds_addr(buf + mf::kLatBytes + (key_l >> 3) * 1024 + (key_l & 7) * 16 + g2 * 128);
+  const uint32_t qr = lds_addr(qrope + g2 * (kMfmaRows * 16));
+  f32x16_t sacc;
+  bf16x8_t k0, k1, k2, k3, k4, k5, r0, r1, r2, r3;
+  asm volatile(TV_QK_ASM
+               : [s] "=&v"(sacc), [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2), [k3] "=&v"(k3), [k4] "=&v"(k4),
+                 [k5] "=&v"(k5), [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3)
+               : [lat] "v"(lat), [rope] "v"(rope), [qr] "v"(qr), [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]),
+                 [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]),
+                 [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),
+                 [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), [q18] "v"(qf[18]),
+                 [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), [q22] "v"(qf[22]), [q23] "v"(qf[23]),
+                 [q24] "v"(qf[24]), [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]),
+                 [q29] "v"(qf[29]), [q30] "v"(qf[30]), [q31] "v"(qf[31])
+               : "memory");
   float s[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) s[i] = sacc[i];
 
-  // ---- mask: register i holds key kt + 8 (i/4) + 4 g2 + i%4.
+  // Mask: register i holds key kt + 8 (i/4) + 4 g2 + i%4.
   if (kt + kMfmaKeys > P || kt + kMfmaKeys > k_end) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -128,7 +172,7 @@ __device__ __forceinline__ void tile_compute(const unsigned char* buf, const bf1
     }
   }
 
-  // ---- softmax weights (base 2) against the row's reference max.
+  // Softmax weights (base 2) against the row's reference max.
   float mt = s[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
@@ -137,38 +181,76 @@ __device__ __forceinline__ void tile_compute(const unsigned char* buf, const bf1
   if (st.m_ref == -INFINITY) st.m_ref = mt;  // first visible tile: o and l are still 0
   st.over = st.over || (mt > st.m_ref + mf::kHeadroom);
   const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
-  bf16x8_t p0, p1;
-  float lsum = 0.f;
+  // v_exp_f32 directly: arguments are <= 64 (or -inf for masked keys, giving
+  // 0); results below the normal range may flush to 0, which only drops keys
+  // weighing < 2^-126 of the reference.
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    p0[i] = static_cast<__bf16>(exp2f(s[i] - mref));
-    p1[i] = static_cast<__bf16>(exp2f(s[i + 8] - mref));
+    p0[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[i] - mref));
+    p1[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[i + 8] - mref));
   }
+  // The denominator sums the rounded weights the value product uses, two at a
+  // time with a bf16 dot product against (1, 1).
+  const bf16x2_t one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float lsum = st.l;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lsum += static_cast<float>(p0[i]) + static_cast<float>(p1[i]);
-  st.l += lsum;
+  for (int i = 0; i < 8; i += 2) {
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{p0[i], p0[i + 1]}, one2, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{p1[i], p1[i + 1]}, one2, lsum, false);
+  }
+  st.l = lsum;
+}
 
-  // ---- O^T += V^T P^T: 16 d-blocks x 2 key halves.  The A operand (V^T) comes
-  // from the row-major tile through ds_read_b64_tr_b16: in each 16-lane group,
-  // lane j points at 4 consecutive d of key row kb + j/4, and receives back the
-  // 4 keys kb .. kb+3 of d = d0 + j.
+// O^T += V^T P^T for one tile: 16 d-blocks x 2 key halves, A operand read from
+// the transposed tile with ds_read_b128, 4 MFMAs ahead.
+__device__ __forceinline__ void pv(const unsigned char* vt, WaveState& st, int lane, const bf16x8_t& p0,
+                                   const bf16x8_t& p1) {
+  const int g2 = lane >> 5;
+  const int dl = lane & 31;
+  // 32 MFMAs (TV_PV_ASM, generated); MFMA n = 2 db + h reads V^T at a_h + 2048 db.
+  const uint32_t a0 = lds_addr(vt + vt_offset(dl, g2));
+  const uint32_t a1 = lds_addr(vt + vt_offset(dl, 2 + g2));
+  bf16x8_t v0, v1, v2, v3, v4, v5;
+  asm volatile(TV_PV_ASM
+               : [o0] "+a"(st.o[0]), [o1] "+a"(st.o[1]), [o2] "+a"(st.o[2]), [o3] "+a"(st.o[3]), [o4] "+a"(st.o[4]),
+                 [o5] "+a"(st.o[5]), [o6] "+a"(st.o[6]), [o7] "+a"(st.o[7]), [o8] "+a"(st.o[8]), [o9] "+a"(st.o[9]),
+                 [o10] "+a"(st.o[10]), [o11] "+a"(st.o[11]), [o12] "+a"(st.o[12]), [o13] "+a"(st.o[13]),
+                 [o14] "+a"(st.o[14]), [o15] "+a"(st.o[15]), [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2),
+                 [v3] "=&v"(v3), [v4] "=&v"(v4), [v5] "=&v"(v5)
+               : [a0] "v"(a0), [a1] "v"(a1), [p0] "v"(p0), [p1] "v"(p1)
+               : "memory");
+}
+
+// The value product of this tile with this wave's quarter of the next tile's
+// transpose (kn -> vn, as transpose_quarter) woven into the MFMA chain.
+__device__ __forceinline__ void pv_transpose(const unsigned char* vt, const unsigned char* kn, unsigned char* vn,
+                                             WaveState& st, int lane, int wave, const bf16x8_t& p0,
+                                             const bf16x8_t& p1) {
+  const int g2 = lane >> 5;
+  const int dl = lane & 31;
   const int grp = lane >> 4;
   const int j = lane & 15;
+  const uint32_t a0 = lds_addr(vt + vt_offset(dl, g2));
+  const uint32_t a1 = lds_addr(vt + vt_offset(dl, 2 + g2));
   const int d0 = 16 * (grp & 1) + 4 * (j & 3);
-  const unsigned char* vbase = buf + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + d0 * 2;
-#pragma unroll
-  for (int db = 0; db < 16; ++db) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const unsigned char* va = vbase + (16 * h) * mf::kLatRowBytes + db * 64;
-      const unsigned char* vb = va + 8 * mf::kLatRowBytes;
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(va));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(vb));
-      const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8_t v = __builtin_bit_cast(bf16x8_t, both);
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, h ? p1 : p0, st.o[db], 0, 0, 0);
-    }
-  }
+  const uint32_t tb = lds_addr(kn + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + d0 * 2 + 256 * wave);
+  const uint32_t wb0 = lds_addr(vn + vt_offset(dl, g2) + 8192 * wave);
+  const uint32_t wb1 = lds_addr(vn + vt_offset(dl, 2 + g2) + 8192 * wave);
+  bf16x8_t v0, v1, v2, v3, v4, v5;
+  i16x4_t t0lo, t0hi, t1lo, t1hi, t2lo, t2hi, t3lo, t3hi, t4lo, t4hi, t5lo, t5hi, t6lo, t6hi, t7lo, t7hi;
+  asm volatile(TV_PV_TRANSPOSE_ASM
+               : [o0] "+a"(st.o[0]), [o1] "+a"(st.o[1]), [o2] "+a"(st.o[2]), [o3] "+a"(st.o[3]), [o4] "+a"(st.o[4]),
+                 [o5] "+a"(st.o[5]), [o6] "+a"(st.o[6]), [o7] "+a"(st.o[7]), [o8] "+a"(st.o[8]), [o9] "+a"(st.o[9]),
+                 [o10] "+a"(st.o[10]), [o11] "+a"(st.o[11]), [o12] "+a"(st.o[12]), [o13] "+a"(st.o[13]),
+                 [o14] "+a"(st.o[14]), [o15] "+a"(st.o[15]), [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2),
+                 [v3] "=&v"(v3), [v4] "=&v"(v4), [v5] "=&v"(v5), [t0lo] "=&v"(t0lo), [t0hi] "=&v"(t0hi),
+                 [t1lo] "=&v"(t1lo), [t1hi] "=&v"(t1hi), [t2lo] "=&v"(t2lo), [t2hi] "=&v"(t2hi),
+                 [t3lo] "=&v"(t3lo), [t3hi] "=&v"(t3hi), [t4lo] "=&v"(t4lo), [t4hi] "=&v"(t4hi),
+                 [t5lo] "=&v"(t5lo), [t5hi] "=&v"(t5hi), [t6lo] "=&v"(t6lo), [t6hi] "=&v"(t6hi),
+                 [t7lo] "=&v"(t7lo), [t7hi] "=&v"(t7hi)
+               : [a0] "v"(a0), [a1] "v"(a1), [p0] "v"(p0), [p1] "v"(p1), [tb] "v"(tb), [wb0] "v"(wb0),
+                 [wb1] "v"(wb1)
+               : "memory");
 }
 
 __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArgs a) {
@@ -186,9 +268,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   const uint16_t* ckv_b = static_cast<const uint16_t*>(a.c_kv) + static_cast<int64_t>(b) * a.kv_len * mf::DC;
   const uint16_t* krope_b = static_cast<const uint16_t*>(a.k_rope) + static_cast<int64_t>(b) * a.kv_len * mf::DR;
 
-  // First tile in flight while the prologue runs.
   const int n_tiles = (w.k_end - w.k_begin + kMfmaKeys - 1) / kMfmaKeys;
-  stage_tile(g_kv_buf0, ckv_b, krope_b, w.k_begin, w.k_end, wave, lane);
+  auto stage = [&](unsigned char* buf, int t) {
+    stage_tile(buf, ckv_b, krope_b, w.k_begin + t * kMfmaKeys, w.k_end, wave, lane);
+  };
 
   build_ancestors(a.parent + static_cast<int64_t>(b) * a.q_len, a.q_len, s_par, s_anc);
 
@@ -236,25 +319,40 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   WaveState st;
   st.m_ref = -INFINITY;
   st.m_seen = -INFINITY;
+  // One tile step.  On entry (after the first barrier) tile t is in kc and its
+  // transpose in vc; tile t+1 is in flight to kn.  After the second barrier
+  // tile t+1 has landed and kc is free, so tile t+2 is sent to kc while the
+  // waves run the value product on vc and transpose tile t+1 into vn.
+  auto step = [&](int t, unsigned char* kc, unsigned char* kn, unsigned char* vc, unsigned char* vn) {
+    // Every wave computes (a wave past the last row works on zero queries and
+    // stores nothing), since all four share the transposes.
+    bf16x8_t p0, p1;
+    __syncthreads();
+    qk_softmax(kc, qf, qrope, st, lane, w.k_begin + t * kMfmaKeys, w.k_end, P, anc, p0, p1);
+    // Tile t+1 (this wave's share, sent one step ago) must have landed in kn
+    // before the barrier: the transpose below reads all of it.  The barrier
+    // alone only drains LDS instructions, not the HBM->LDS copies, and the
+    // compiler cannot see the LDS reads inside the asm blocks.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < n_tiles) stage(kc, t + 2);
+    // On the last tile the transpose of kn into vn is idle work on a buffer
+    // nobody reads again; doing it anyway keeps a single code path.
+    pv_transpose(vc, kn, vn, st, lane, wave, p0, p1);
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int db = 0; db < 16; ++db) st.o[db] = f32x16_t{};
     st.l = 0.f;
     st.over = false;
-    if (pass > 0) stage_tile(g_kv_buf0, ckv_b, krope_b, w.k_begin, w.k_end, wave, lane);
-    for (int t = 0; t < n_tiles; t += 2) {
-      // tile t in buf0
-      __syncthreads();  // buf0's copy landed (each wave waited for its own), buf1 free
-      if (t + 1 < n_tiles)
-        stage_tile(g_kv_buf1, ckv_b, krope_b, w.k_begin + (t + 1) * kMfmaKeys, w.k_end, wave, lane);
-      if (wave_active) tile_compute(g_kv_buf0, qf, qrope, st, lane, w.k_begin + t * kMfmaKeys, w.k_end, P, anc);
-      if (t + 1 >= n_tiles) break;
-      // tile t + 1 in buf1
-      __syncthreads();
-      if (t + 2 < n_tiles)
-        stage_tile(g_kv_buf0, ckv_b, krope_b, w.k_begin + (t + 2) * kMfmaKeys, w.k_end, wave, lane);
-      if (wave_active)
-        tile_compute(g_kv_buf1, qf, qrope, st, lane, w.k_begin + (t + 1) * kMfmaKeys, w.k_end, P, anc);
+    stage(g_k0, 0);
+    if (n_tiles > 1) stage(g_k1, 1);
+    __syncthreads();
+    transpose_quarter(g_k0, g_vt0, lane, wave);
+    for (int t = 0; t < n_tiles; ++t) {
+      const bool odd = t & 1;
+      step(t, odd ? g_k1 : g_k0, odd ? g_k0 : g_k1, odd ? g_vt1 : g_vt0, odd ? g_vt0 : g_vt1);
     }
     // Re-sweep (once, with the exact max as reference) if any row overflowed headroom.
     if (threadIdx.x == 0) s_redo = 0;
