@@ -98,6 +98,20 @@ def load_traffic(kernel: dict, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def copy_calibration(torch) -> int:
+    """A plain copy of known size: each launch reads and writes exactly 1 GiB."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "launches": 3, "bytes_read_per_launch": 4 * n,
+                      "bytes_written_per_launch": 4 * n}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +119,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-sample", type=int, default=6, help="trees the CPU oracle times (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (the reference launch that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -116,6 +133,9 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        return copy_calibration(torch)
 
     from tree_verify_mla_tv_amd import tv
     from tree_verify_mla_tv_amd import workloads as W

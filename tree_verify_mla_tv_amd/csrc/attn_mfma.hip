@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g2 = lane >> 5;
-  const Unit w = decode_unit(a, blockIdx.x);
+  const Unit w = decode_unit(a, unit_of_block(a, blockIdx.x));
   const int b = w.b;
   const int P = a.prefix_len;
   const uint16_t* ckv_b = static_cast<const uint16_t*>(a.c_kv) + static_cast<int64_t>(b) * a.kv_len * mf::DC;

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   __shared__ unsigned long long s_anc[kMaxQ];
 
   const int tid = threadIdx.x;
-  const Unit w = decode_unit(a, blockIdx.x);
+  const Unit w = decode_unit(a, unit_of_block(a, blockIdx.x));
   const int b = w.b;
   const int r0 = w.rb * kValuRows;
   const int k_begin = w.k_begin;

@@ -120,6 +120,25 @@ __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long long u) {
   return w;
 }
 
+// Workgroup x of a launch runs on XCD x % 8 (the hardware deals workgroups to
+// the 8 XCDs in turn), and each XCD has its own L2.  Units are numbered tree by
+// tree, full row blocks first, then the pieces of the split tail blocks; this
+// order gives each XCD a contiguous run of full-block units and then a
+// contiguous run of pieces, so the workgroups sharing a tree's latent rows
+// mostly share one L2.  It is a bijection on [0, units): within each of the
+// two ranges the first multiple of 8 is dealt XCD by XCD, the rest in order.
+__device__ __forceinline__ long long unit_of_block(const AttnArgs& a, long long x) {
+  constexpr int kXcds = 8;
+  const long long units_full = static_cast<long long>(a.B) * a.full_rb * a.split_full;
+  const long long f8 = units_full / kXcds * kXcds;
+  if (x < f8) return (x % kXcds) * (f8 / kXcds) + x / kXcds;
+  const long long p = x - f8;
+  const long long units = units_full + (a.full_rb < a.n_rb ? static_cast<long long>(a.B) * a.split_tail : 0);
+  const long long r8 = (units - f8) / kXcds * kXcds;
+  if (p < r8) return f8 + (p % kXcds) * (r8 / kXcds) + p / kXcds;
+  return x;
+}
+
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 
 // Kernel launchers (one per kernel family).
