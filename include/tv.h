@@ -109,7 +109,9 @@ tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t 
  *     parent [B][q_len] int32
  *     out    [B][q_len][H][d_c] f32      lse    [B][q_len][H] f32, or NULL
  *   Supported (d_c, d_r, kv_dtype): d_c in {64, 128, 256, 512}, d_r in {32, 64},
- *   kv_dtype TV_F32 or TV_BF16.  1 <= q_len <= TV_MAX_Q_LEN.
+ *   kv_dtype TV_F32 or TV_BF16.  1 <= q_len <= TV_MAX_Q_LEN.  One tree's
+ *   latent rows (kv_len * d_c elements of kv_dtype) must stay below 2^31
+ *   bytes (TV_ERR_UNSUPPORTED otherwise).
  *   workspace: caller-owned device scratch of at least
  *   tv_verify_attn_workspace_size(...) bytes (NULL allowed when that is 0).
  *   out must not overlap any input.

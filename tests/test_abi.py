@@ -60,6 +60,8 @@ def _attn(lib, **kw):
     (dict(q_lat=A + 8), INV), (dict(c_kv=A + 4), INV), (dict(out=A + 12), INV), (dict(parent=A + 2), INV),
     (dict(lse=A + 1), INV), (dict(scale=float("inf")), INV), (dict(scale=float("nan")), INV),
     (dict(prefix=2**31 - 10), INV),
+    # one tree's latent rows at 2^31 bytes: bf16 at kv_len 2^21, f32 at 2^20
+    (dict(prefix=2**21 - 3, d_c=512, dt=1), UNS), (dict(prefix=2**20 - 3, d_c=512, dt=0), UNS),
 ])
 def test_verify_attn_rejects_before_launch(kw, code):
     assert _attn(tv.load(), **kw) == code

@@ -10,35 +10,36 @@
 // product and a dense [R x kv] x [kv x 512] output product.  Those two products
 // run on v_mfma_f32_32x32x16_bf16; the rest (mask, softmax) is VALU work.
 //
-// Workgroup = 4 waves, one per SIMD; wave w owns 32 query rows.  Per wave:
-//   * its 32 query rows live in registers for the whole kv sweep, pre-scaled by
-//     sm_scale * log2(e) and rounded once to bf16 (144 VGPRs, the B operand of
-//     S^T = K Q^T);
-//   * the 32 x 512 fp32 output block lives in 256 accumulator registers
-//     (O^T = V^T P^T, so a lane owns one query row in both products and the
-//     softmax state is lane-local);
-// Per kv tile of 32 latent rows (shared by all 4 waves through LDS):
-//   * the tile is copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
-//     round trip), double-buffered so tile t+1 streams in while tile t is used;
-//   * QK reads the tile row-major (ds_read_b128); PV reads the same bytes
-//     transposed with ds_read_b64_tr_b16, so no second, transposed copy exists;
-//   * softmax is online in base 2 against a per-row reference max fixed by the
-//     first tile the row sees; the accumulators are never rescaled.  Weights
-//     exp2(s - m_ref) may exceed 1 (fp32 and bf16 carry them exactly as well);
-//     if some later score exceeds m_ref by more than 2^64 the workgroup sweeps
-//     its kv range once more, with m_ref = the exact row max for the rows that
-//     ran out of headroom, so nothing overflows for any finite input.
-// Scores of a tile that holds tree rows are masked by the ancestor bit mask.
+// Workgroup = 4 waves, one per SIMD, 128 query rows (row blocks rb = 0..3 of
+// 32 rows).  Wave w
+//   * computes the scores and softmax weights of row block w: its 32 query rows
+//     live in registers for the whole kv sweep, pre-scaled by
+//     sm_scale * log2(e) and rounded once to bf16 (the B operand of
+//     S^T = K Q^T), and the weights go to LDS for all four waves;
+//   * accumulates output columns 128 w .. 128 w + 127 of all 128 rows:
+//     O^T[rb][db] = V^T P^T in 16 x 16 fp32 accumulator registers per lane
+//     (all 256), with V^T read straight from the row-major tile by
+//     ds_read_b64_tr_b16 (no transposed copy).
+// So each latent fragment read from LDS feeds four matrix ops, and the
+// accumulators are never rescaled: the softmax is online in base 2 against a
+// per-row reference max fixed by the first tile the row sees.  Weights
+// exp2(s - m_ref) may exceed 1 (fp32 and bf16 carry them exactly as well); if
+// some later score exceeds m_ref by more than 2^64 the workgroup sweeps its kv
+// range once more, with m_ref = the exact row max for the rows that ran out of
+// headroom, so nothing overflows for any finite input.
+//
+// Step t of the sweep (one barrier): the copy of tile t+1 HBM -> LDS starts
+// (global_load_lds_dwordx4, three tile buffers in rotation); scores of tile t
+// (TV_QK_ASM); mask and row max; then one asm block (TV_PVS_ASM) runs the
+// value product of tile t-1 and, woven between its matrix ops, the
+// exponentials, bf16 packing, row sums and LDS stores of tile t's weights.
 #include "tv_kernels.h"
 #include "attn_mfma_asm.h"
 
 namespace tv {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(4))) short i16x4_t;
-typedef __attribute__((ext_vector_type(8))) short i16x8_t;
 
 namespace mf {
 constexpr int DC = 512, DR = 64, D = DC + DR;
@@ -49,97 +50,90 @@ constexpr int kLatRowBytes = DC * 2 + kPadBytes;    // 1040
 constexpr int kLatBytes = kMfmaKeys * kLatRowBytes; // 33280
 constexpr int kRopeBytes = kMfmaKeys * DR * 2;      // 4096
 constexpr int kBufBytes = kLatBytes + kRopeBytes;   // 37376
-constexpr int kVtBytes = DC * 64;                   // 32768: V^T tile, 512 rows of 32 keys
+constexpr int kPBytes = kMfmaRows * kMfmaKeys * 2;  // 8192: one tile's bf16 weights
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kHeadroom = 64.0f;                  // log2 units above m_ref before a re-sweep
 }  // namespace mf
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
-typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr_t;
 
 // 32-bit LDS address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
 }
 
-// Two kv tiles (row-major, as in HBM) and two transposed latent tiles.
+// Three kv tile buffers (row-major, as in HBM), used in rotation.
 __shared__ __align__(16) unsigned char g_k0[mf::kBufBytes];
 __shared__ __align__(16) unsigned char g_k1[mf::kBufBytes];
-__shared__ __align__(16) unsigned char g_vt0[mf::kVtBytes];
-__shared__ __align__(16) unsigned char g_vt1[mf::kVtBytes];
+__shared__ __align__(16) unsigned char g_k2[mf::kBufBytes];
+// Softmax weights of two consecutive tiles: [rb][key half h][lane][8 x bf16],
+// lane l holding row 32 rb + l % 32 and keys 16 h + {4 g .. 4 g + 3,
+// 8 + 4 g .. 8 + 4 g + 3} (g = l / 32) -- the B operand of the value MFMA.
+__shared__ __align__(16) unsigned char g_p[2][mf::kPBytes];
 
-// Copy kv rows [kt, kt + 32) of one tree into a row-major tile buffer.  Rows
-// past k_end repeat row k_end - 1 (finite data; their scores are masked).
+// Copy kv rows [kt, kt + 32) of one tree into a tile buffer.  Rows past k_end
+// repeat row k_end - 1 (finite data; their scores are masked).
 //   latent rows:  row k at buf + k * kLatRowBytes, 64 chunks of 16 B; wave w
 //                 copies rows 8w .. 8w+7, one wave-wide 1 KB copy per row.
 //   rope rows:    wave w copies keys 8w .. 8w+7 into buf + kLatBytes + 1024 w,
 //                 chunk-major: 16-byte chunk c of key k at slot c * 8 + (k % 8).
-__device__ __forceinline__ void stage_tile(unsigned char* buf, const uint16_t* __restrict__ ckv_b,
-                                           const uint16_t* __restrict__ krope_b, int kt, int k_end, int wave,
-                                           int lane) {
+// Buffer loads straight to LDS (buffer_load_dwordx4 ... lds): the tree's base
+// is in the scalar resource, the row in a scalar offset, and each lane adds its
+// 16-byte chunk (lane16 = 16 * lane), so a copy costs no address registers.
+// Nine loads per wave; the caller waits for them (vmcnt) before the barrier
+// that publishes the tile.
+struct TreeKv {
+  __amdgpu_buffer_rsrc_t lat;   // c_kv rows of the tree, 1024 B each
+  __amdgpu_buffer_rsrc_t rope;  // k_rope rows of the tree, 128 B each
+};
+
+__device__ __forceinline__ void stage_tile(unsigned char* buf, const TreeKv& kv, int kt, int k_end, int wave,
+                                           int lane, uint32_t lane16) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int k = wave * 8 + r;
     const int key = min(kt + k, k_end - 1);
-    const uint16_t* src = ckv_b + static_cast<int64_t>(key) * mf::DC + lane * 8;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src), (lds_ptr_t)(buf + k * mf::kLatRowBytes), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kv.lat, (lds_ptr_t)(buf + k * mf::kLatRowBytes), 16, lane16,
+                                             key * (mf::DC * 2), 0, 0);
   }
   const int c = lane >> 3;
   const int kl = lane & 7;
   const int key = min(kt + wave * 8 + kl, k_end - 1);
-  const uint16_t* src = krope_b + static_cast<int64_t>(key) * mf::DR + c * 8;
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src), (lds_ptr_t)(buf + mf::kLatBytes + wave * 1024), 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(kv.rope, (lds_ptr_t)(buf + mf::kLatBytes + wave * 1024), 16,
+                                           key * (mf::DR * 2) + c * 16, 0, 0, 0);
 }
 
-// Transposed latent tile V^T: 512 rows d of 4 chunks of 16 B.  Chunk 2h + g of
-// row d holds the 8 keys 16 h + {4 g .. 4 g + 3, 8 + 4 g .. 8 + 4 g + 3} at d,
-// i.e. exactly the A operand lane (d % 32) + 32 g needs for the value MFMA of
-// key half h.  Chunks are XOR-swizzled by (d >> 2) & 3 so the 16 lanes of a
-// 128-bit access hit 16 different bank groups.
-__device__ __forceinline__ int vt_offset(int d, int chunk) { return d * 64 + 16 * (chunk ^ ((d >> 2) & 3)); }
-
-// One wave's quarter of the transpose of a row-major tile (d-blocks 4w..4w+3)
-// into V^T, through ds_read_b64_tr_b16: in each 16-lane group, lane j points at
-// 4 consecutive d of key row kb + j/4 and receives the 4 keys kb .. kb+3 of
-// d = d0 + j.
-__device__ __forceinline__ void transpose_quarter(const unsigned char* kbuf, unsigned char* vt, int lane, int wave) {
-  const int g2 = lane >> 5;
-  const int grp = lane >> 4;
-  const int j = lane & 15;
-  const int d0 = 16 * (grp & 1) + 4 * (j & 3);
-  const unsigned char* vbase = kbuf + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + d0 * 2;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int db = 4 * wave + (u >> 1);
-    const int h = u & 1;
-    const unsigned char* va = vbase + (16 * h) * mf::kLatRowBytes + db * 64;
-    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(va));
-    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(va + 8 * mf::kLatRowBytes));
-    const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    *reinterpret_cast<i16x8_t*>(vt + vt_offset(32 * db + (lane & 31), 2 * h + g2)) = v;
-  }
-}
-
-// Everything one wave keeps across tiles.
-struct WaveState {
-  f32x16_t o[16];   // O^T blocks: o[db][i] = out[row][32 db + 8 (i/4) + 4 g2 + i%4]
-  float m_ref;      // reference max (log2 units) the exponentials are taken against
-  float m_seen;     // exact running max of the row's visible scores (log2 units)
-  float l;          // this lane's share of the row's softmax denominator
-  bool over;        // a score exceeded m_ref + kHeadroom
+// Per-lane row state of the softmax (rows of the wave's own row block).
+struct RowState {
+  float m_ref;   // reference max (log2 units) the exponentials are taken against
+  float m_seen;  // exact running max of the row's visible scores (log2 units)
+  float l;       // this lane's share of the row's softmax denominator
+  bool over;     // a score exceeded m_ref + kHeadroom
 };
 
-// S^T = K Q^T for one tile, mask, and the tile's softmax weights (bf16).
-__device__ __forceinline__ void qk_softmax(const unsigned char* buf, const bf16x8_t* qf, const unsigned char* qrope,
-                                           WaveState& st, int lane, int kt, int k_end, int P,
-                                           unsigned long long anc, bf16x8_t& p0, bf16x8_t& p1) {
+// Lanes l and l + 32 hold the same row: swap the wave's halves and combine.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// S^T = K Q^T for one tile (lane: row lane % 32, keys 8 (i/4) + 4 g + i % 4 in
+// register i), masked, and the row's max folded into the state.  Returns the
+// reference the exponentials are taken against.
+__device__ __forceinline__ float scores(const unsigned char* buf, const bf16x8_t* qf, const unsigned char* qrope,
+                                        RowState& st, int lane, int kt, int k_end, int P, unsigned long long anc,
+                                        float (&s)[16]) {
   const int g2 = lane >> 5;
   const int key_l = lane & 31;
-  // 36 MFMAs 32x32x16 in one accumulator chain (TV_QK_ASM, generated): the
-  // latent part of Q is in registers (qf), the rope part in LDS (qrope,
-  // chunk-major); every K fragment is read 4 MFMAs ahead of its use.
+  // 36 MFMAs 32x32x16 in one accumulator chain: the latent part of Q is in
+  // registers (qf), the rope part in LDS (qrope, chunk-major); every K
+  // fragment is read 4 MFMAs ahead of its use.
   const uint32_t lat = lds_addr(buf + key_l * mf::kLatRowBytes + g2 * 16);
   const uint32_t rope = lds_addr(buf + mf::kLatBytes + (key_l >> 3) * 1024 + (key_l & 7) * 16 + g2 * 128);
   const uint32_t qr = lds_addr(qrope + g2 * (kMfmaRows * 16));
@@ -156,11 +150,10 @@ __device__ __forceinline__ void qk_softmax(const unsigned char* buf, const bf16x
                  [q24] "v"(qf[24]), [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]),
                  [q29] "v"(qf[29]), [q30] "v"(qf[30]), [q31] "v"(qf[31])
                : "memory");
-  float s[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) s[i] = sacc[i];
 
-  // Mask: register i holds key kt + 8 (i/4) + 4 g2 + i%4.
+  // Mask (only tiles reaching past the prefix or the unit's kv range).
   if (kt + kMfmaKeys > P || kt + kMfmaKeys > k_end) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -172,91 +165,58 @@ __device__ __forceinline__ void qk_softmax(const unsigned char* buf, const bf16x
     }
   }
 
-  // Softmax weights (base 2) against the row's reference max.
   float mt = s[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32));  // lanes l and l ^ 32 hold the same row
+  mt = max_halves(mt);
   st.m_seen = fmaxf(st.m_seen, mt);
-  if (st.m_ref == -INFINITY) st.m_ref = mt;  // first visible tile: o and l are still 0
+  if (st.m_ref == -INFINITY) st.m_ref = mt;  // first visible tile: nothing accumulated yet
   st.over = st.over || (mt > st.m_ref + mf::kHeadroom);
-  const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
-  // v_exp_f32 directly: arguments are <= 64 (or -inf for masked keys, giving
-  // 0); results below the normal range may flush to 0, which only drops keys
-  // weighing < 2^-126 of the reference.
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p0[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[i] - mref));
-    p1[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[i + 8] - mref));
-  }
-  // The denominator sums the rounded weights the value product uses, two at a
-  // time with a bf16 dot product against (1, 1).
-  const bf16x2_t one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  float lsum = st.l;
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{p0[i], p0[i + 1]}, one2, lsum, false);
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{p1[i], p1[i + 1]}, one2, lsum, false);
-  }
-  st.l = lsum;
+  return st.m_ref == -INFINITY ? 0.f : st.m_ref;
 }
 
-// O^T += V^T P^T for one tile: 16 d-blocks x 2 key halves, A operand read from
-// the transposed tile with ds_read_b128, 4 MFMAs ahead.
-__device__ __forceinline__ void pv(const unsigned char* vt, WaveState& st, int lane, const bf16x8_t& p0,
-                                   const bf16x8_t& p1) {
+// O^T += V^T P^T for the previous tile (kp, weights pp) with this tile's
+// softmax (scores s against mref, weights to pc) woven in.  v_exp_f32 is used
+// directly: its arguments are <= 64 or -inf (masked keys, giving 0), and
+// results below the normal range may flush to 0, which only drops keys
+// weighing < 2^-126 of the reference.
+__device__ __forceinline__ void value_and_softmax(const unsigned char* kp, const unsigned char* pp, unsigned char* pc,
+                                                  f32x16_t (&o)[16], float (&s)[16], float mref, float& l,
+                                                  int lane, int wave) {
   const int g2 = lane >> 5;
-  const int dl = lane & 31;
-  // 32 MFMAs (TV_PV_ASM, generated); MFMA n = 2 db + h reads V^T at a_h + 2048 db.
-  const uint32_t a0 = lds_addr(vt + vt_offset(dl, g2));
-  const uint32_t a1 = lds_addr(vt + vt_offset(dl, 2 + g2));
-  bf16x8_t v0, v1, v2, v3, v4, v5;
-  asm volatile(TV_PV_ASM
-               : [o0] "+a"(st.o[0]), [o1] "+a"(st.o[1]), [o2] "+a"(st.o[2]), [o3] "+a"(st.o[3]), [o4] "+a"(st.o[4]),
-                 [o5] "+a"(st.o[5]), [o6] "+a"(st.o[6]), [o7] "+a"(st.o[7]), [o8] "+a"(st.o[8]), [o9] "+a"(st.o[9]),
-                 [o10] "+a"(st.o[10]), [o11] "+a"(st.o[11]), [o12] "+a"(st.o[12]), [o13] "+a"(st.o[13]),
-                 [o14] "+a"(st.o[14]), [o15] "+a"(st.o[15]), [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2),
-                 [v3] "=&v"(v3), [v4] "=&v"(v4), [v5] "=&v"(v5)
-               : [a0] "v"(a0), [a1] "v"(a1), [p0] "v"(p0), [p1] "v"(p1)
-               : "memory");
-}
-
-// The value product of this tile with this wave's quarter of the next tile's
-// transpose (kn -> vn, as transpose_quarter) woven into the MFMA chain.
-__device__ __forceinline__ void pv_transpose(const unsigned char* vt, const unsigned char* kn, unsigned char* vn,
-                                             WaveState& st, int lane, int wave, const bf16x8_t& p0,
-                                             const bf16x8_t& p1) {
-  const int g2 = lane >> 5;
-  const int dl = lane & 31;
   const int grp = lane >> 4;
   const int j = lane & 15;
-  const uint32_t a0 = lds_addr(vt + vt_offset(dl, g2));
-  const uint32_t a1 = lds_addr(vt + vt_offset(dl, 2 + g2));
-  const int d0 = 16 * (grp & 1) + 4 * (j & 3);
-  const uint32_t tb = lds_addr(kn + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + d0 * 2 + 256 * wave);
-  const uint32_t wb0 = lds_addr(vn + vt_offset(dl, g2) + 8192 * wave);
-  const uint32_t wb1 = lds_addr(vn + vt_offset(dl, 2 + g2) + 8192 * wave);
-  bf16x8_t v0, v1, v2, v3, v4, v5;
-  i16x4_t t0lo, t0hi, t1lo, t1hi, t2lo, t2hi, t3lo, t3hi, t4lo, t4hi, t5lo, t5hi, t6lo, t6hi, t7lo, t7hi;
-  asm volatile(TV_PV_TRANSPOSE_ASM
-               : [o0] "+a"(st.o[0]), [o1] "+a"(st.o[1]), [o2] "+a"(st.o[2]), [o3] "+a"(st.o[3]), [o4] "+a"(st.o[4]),
-                 [o5] "+a"(st.o[5]), [o6] "+a"(st.o[6]), [o7] "+a"(st.o[7]), [o8] "+a"(st.o[8]), [o9] "+a"(st.o[9]),
-                 [o10] "+a"(st.o[10]), [o11] "+a"(st.o[11]), [o12] "+a"(st.o[12]), [o13] "+a"(st.o[13]),
-                 [o14] "+a"(st.o[14]), [o15] "+a"(st.o[15]), [v0] "=&v"(v0), [v1] "=&v"(v1), [v2] "=&v"(v2),
-                 [v3] "=&v"(v3), [v4] "=&v"(v4), [v5] "=&v"(v5), [t0lo] "=&v"(t0lo), [t0hi] "=&v"(t0hi),
-                 [t1lo] "=&v"(t1lo), [t1hi] "=&v"(t1hi), [t2lo] "=&v"(t2lo), [t2hi] "=&v"(t2hi),
-                 [t3lo] "=&v"(t3lo), [t3hi] "=&v"(t3hi), [t4lo] "=&v"(t4lo), [t4hi] "=&v"(t4hi),
-                 [t5lo] "=&v"(t5lo), [t5hi] "=&v"(t5hi), [t6lo] "=&v"(t6lo), [t6hi] "=&v"(t6hi),
-                 [t7lo] "=&v"(t7lo), [t7hi] "=&v"(t7hi)
-               : [a0] "v"(a0), [a1] "v"(a1), [p0] "v"(p0), [p1] "v"(p1), [tb] "v"(tb), [wb0] "v"(wb0),
-                 [wb1] "v"(wb1)
-               : "memory");
+  // ds_read_b64_tr_b16: in each 16-lane group lane j points at 4 consecutive
+  // latent columns of key row 4 g + j / 4 and receives, for column
+  // 16 (grp & 1) + j, the 4 keys of those rows.
+  const uint32_t tb =
+      lds_addr(kp + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + (16 * (grp & 1) + 4 * (j & 3)) * 2 + 256 * wave);
+  const uint32_t pb = lds_addr(pp + lane * 16);
+  const uint32_t pw0 = lds_addr(pc + wave * 2048 + lane * 16);
+  const uint32_t pw1 = pw0 + 1024;
+  bf16x8_t pi0, pi1, pi2, pi3, pi4, pi5, pi6, pi7;
+  uint32_t pk0, pk1, pk2, pk3, pk4, pk5, pk6, pk7;
+  asm volatile(TV_PVS_ASM
+               : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),
+                 [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),
+                 [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]),
+                 [o15] "+a"(o[15]), [s0] "+v"(s[0]), [s1] "+v"(s[1]), [s2] "+v"(s[2]), [s3] "+v"(s[3]),
+                 [s4] "+v"(s[4]), [s5] "+v"(s[5]), [s6] "+v"(s[6]), [s7] "+v"(s[7]), [s8] "+v"(s[8]),
+                 [s9] "+v"(s[9]), [s10] "+v"(s[10]), [s11] "+v"(s[11]), [s12] "+v"(s[12]), [s13] "+v"(s[13]),
+                 [s14] "+v"(s[14]), [s15] "+v"(s[15]), [l] "+v"(l), [pi0] "=&v"(pi0), [pi1] "=&v"(pi1),
+                 [pi2] "=&v"(pi2), [pi3] "=&v"(pi3), [pi4] "=&v"(pi4), [pi5] "=&v"(pi5), [pi6] "=&v"(pi6),
+                 [pi7] "=&v"(pi7), [pk0] "=&v"(pk0), [pk1] "=&v"(pk1), [pk2] "=&v"(pk2), [pk3] "=&v"(pk3),
+                 [pk4] "=&v"(pk4), [pk5] "=&v"(pk5), [pk6] "=&v"(pk6), [pk7] "=&v"(pk7)
+               : [mref] "v"(mref), [tb] "v"(tb), [pb] "v"(pb), [pw0] "v"(pw0), [pw1] "v"(pw1)
+               : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251",
+                 "v252", "v253", "v254", "v255", "memory");
 }
 
 __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArgs a) {
   __shared__ int s_par[kMaxQ];
   __shared__ unsigned long long s_anc[kMaxQ];
   __shared__ __align__(16) unsigned char s_qrope[kMfmaRows * mf::DR * 2];  // 16 KB
+  __shared__ float s_row_l[kMfmaRows];
   __shared__ int s_redo;
 
   const int lane = threadIdx.x & 63;
@@ -265,18 +225,27 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   const Unit w = decode_unit(a, unit_of_block(a, blockIdx.x));
   const int b = w.b;
   const int P = a.prefix_len;
-  const uint16_t* ckv_b = static_cast<const uint16_t*>(a.c_kv) + static_cast<int64_t>(b) * a.kv_len * mf::DC;
-  const uint16_t* krope_b = static_cast<const uint16_t*>(a.k_rope) + static_cast<int64_t>(b) * a.kv_len * mf::DR;
+  // Buffer resources over this tree's rows (raw buffers: dword 3 of the
+  // descriptor as for any untyped gfx9 buffer; the host keeps kv_len * 1024
+  // below 2^31, so every offset fits).
+  TreeKv kv;
+  {
+    const uint16_t* ckv_b = static_cast<const uint16_t*>(a.c_kv) + static_cast<int64_t>(b) * a.kv_len * mf::DC;
+    const uint16_t* krope_b = static_cast<const uint16_t*>(a.k_rope) + static_cast<int64_t>(b) * a.kv_len * mf::DR;
+    kv.lat = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ckv_b), 0, a.kv_len * (mf::DC * 2), 0x00020000);
+    kv.rope = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(krope_b), 0, a.kv_len * (mf::DR * 2), 0x00020000);
+  }
+  const uint32_t lane16 = lane * 16;
 
   const int n_tiles = (w.k_end - w.k_begin + kMfmaKeys - 1) / kMfmaKeys;
   auto stage = [&](unsigned char* buf, int t) {
-    stage_tile(buf, ckv_b, krope_b, w.k_begin + t * kMfmaKeys, w.k_end, wave, lane);
+    stage_tile(buf, kv, w.k_begin + t * kMfmaKeys, w.k_end, wave, lane, lane16);
   };
 
   build_ancestors(a.parent + static_cast<int64_t>(b) * a.q_len, a.q_len, s_par, s_anc);
 
+  // This wave's own rows (row block rb = wave).
   const int row0 = w.rb * kMfmaRows + wave * 32;
-  const bool wave_active = row0 < a.R;
   const int row = row0 + (lane & 31);
   const bool row_valid = row < a.R;
   const int node = min(row / a.H, a.q_len - 1);
@@ -284,7 +253,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
 
   // Query fragments: q[row][8 g2 + 16 ks .. + 7] * sm_scale * log2(e) as bf16.
   // Latent part (ks < 32) in registers; rope part in LDS, chunk-major:
-  // 16-byte chunk c of block row r at s_qrope + (c * 128 + r) * 16.
+  // 16-byte chunk c of block row r at s_qrope + (c * 128 + r) * 16.  Rows past
+  // R get zero queries (their results are never stored).
   bf16x8_t qf[mf::KSTEPS_LAT];
   {
     const float sc = a.sm_scale * mf::kLog2e;
@@ -316,48 +286,53 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   }
   const unsigned char* qrope = s_qrope + (wave * 32 + (lane & 31)) * 16;
 
-  WaveState st;
+  f32x16_t o[16];  // o[4 rb + db][i] = O[32 rb + lane % 32][128 wave + 32 db + 8 (i/4) + 4 g2 + i % 4]
+  RowState st;
   st.m_ref = -INFINITY;
   st.m_seen = -INFINITY;
-  // One tile step.  On entry (after the first barrier) tile t is in kc and its
-  // transpose in vc; tile t+1 is in flight to kn.  After the second barrier
-  // tile t+1 has landed and kc is free, so tile t+2 is sent to kc while the
-  // waves run the value product on vc and transpose tile t+1 into vn.
-  auto step = [&](int t, unsigned char* kc, unsigned char* kn, unsigned char* vc, unsigned char* vn) {
-    // Every wave computes (a wave past the last row works on zero queries and
-    // stores nothing), since all four share the transposes.
-    bf16x8_t p0, p1;
-    __syncthreads();
-    qk_softmax(kc, qf, qrope, st, lane, w.k_begin + t * kMfmaKeys, w.k_end, P, anc, p0, p1);
-    // Tile t+1 (this wave's share, sent one step ago) must have landed in kn
-    // before the barrier: the transpose below reads all of it.  The barrier
-    // alone only drains LDS instructions, not the HBM->LDS copies, and the
-    // compiler cannot see the LDS reads inside the asm blocks.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 2 < n_tiles) stage(kc, t + 2);
-    // On the last tile the transpose of kn into vn is idle work on a buffer
-    // nobody reads again; doing it anyway keeps a single code path.
-    pv_transpose(vc, kn, vn, st, lane, wave, p0, p1);
-  };
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int db = 0; db < 16; ++db) st.o[db] = f32x16_t{};
+    for (int i = 0; i < 16; ++i) o[i] = f32x16_t{};
     st.l = 0.f;
     st.over = false;
+    // The weights "before tile 0" are zeros, so step 0's value product adds
+    // nothing (it reads tile 0's finite latent rows).
+    *reinterpret_cast<uint4*>(g_p[1] + threadIdx.x * 32) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(g_p[1] + threadIdx.x * 32 + 16) = make_uint4(0, 0, 0, 0);
     stage(g_k0, 0);
-    if (n_tiles > 1) stage(g_k1, 1);
-    __syncthreads();
-    transpose_quarter(g_k0, g_vt0, lane, wave);
-    for (int t = 0; t < n_tiles; ++t) {
-      const bool odd = t & 1;
-      step(t, odd ? g_k1 : g_k0, odd ? g_k0 : g_k1, odd ? g_vt1 : g_vt0, odd ? g_vt0 : g_vt1);
+    unsigned char* kp = g_k2;  // tile t-1
+    unsigned char* kc = g_k0;  // tile t
+    unsigned char* kn = g_k1;  // tile t+1
+    // Step t: scores of tile t, value product of tile t-1.  The extra step
+    // t = n_tiles only runs the value product of the last tile.
+    for (int t = 0; t <= n_tiles; ++t) {
+      // Tile t (this wave's copies) has landed; after the barrier every wave's
+      // has, the weights of tile t-1 are in LDS, and tile t-2's buffer (kn) and
+      // weights buffer are no longer read.  The barrier alone drains only LDS
+      // instructions, not the HBM->LDS copies, and the compiler cannot see the
+      // LDS reads inside the asm blocks.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t + 1 < n_tiles) stage(kn, t + 1);
+      float s[16];
+      float mref = 0.f;
+      if (t < n_tiles) {
+        mref = scores(kc, qf, qrope, st, lane, w.k_begin + t * kMfmaKeys, w.k_end, P, anc, s);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = -INFINITY;
+      }
+      value_and_softmax(t == 0 ? kc : kp, g_p[(t + 1) & 1], g_p[t & 1], o, s, mref, st.l, lane, wave);
+      unsigned char* nx = kp;
+      kp = kc;
+      kc = kn;
+      kn = nx;
     }
     // Re-sweep (once, with the exact max as reference) if any row overflowed headroom.
     if (threadIdx.x == 0) s_redo = 0;
     __syncthreads();
-    if (wave_active && __any(st.over) && lane == 0) s_redo = 1;
+    if (__any(st.over) && lane == 0) s_redo = 1;
     __syncthreads();
     if (pass > 0 || s_redo == 0) break;
     // Only rows that ran out of headroom move their reference, so every other
@@ -366,30 +341,39 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
     st.m_ref = st.over ? st.m_seen : st.m_ref;
   }
 
-  if (!wave_active) return;
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
-  if (!row_valid) return;
-  const int64_t grow = static_cast<int64_t>(b) * a.R + row;
-  float* dst;
-  if (w.slot < 0) {
-    dst = a.out + grow * mf::DC;
-    if (g2 == 0 && a.lse) a.lse[grow] = (st.m_ref + log2f(l_tot)) * mf::kLn2;
-  } else {
-    const int64_t srow = w.slot * kMfmaRows + (row - w.rb * kMfmaRows);
-    dst = a.ws_o + srow * mf::DC;
-    if (g2 == 0) {
+  // Row sums of the wave's own rows, for all four waves.
+  const float l_tot = sum_halves(st.l);
+  if (g2 == 0) s_row_l[wave * 32 + lane] = l_tot;
+  const int64_t tree_row0 = static_cast<int64_t>(b) * a.R;
+  if (g2 == 0 && row_valid) {
+    if (w.slot < 0) {
+      if (a.lse) a.lse[tree_row0 + row] = (st.m_ref + log2f(l_tot)) * mf::kLn2;
+    } else {
+      const int64_t srow = w.slot * kMfmaRows + wave * 32 + lane;
       a.ws_m[srow] = st.m_ref * mf::kLn2;
       a.ws_l[srow] = l_tot;
     }
   }
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  __syncthreads();
+
 #pragma unroll
-  for (int db = 0; db < 16; ++db) {
+  for (int rb = 0; rb < 4; ++rb) {
+    const int r = w.rb * kMfmaRows + rb * 32 + (lane & 31);
+    if (r < a.R) {
+      const float lr = s_row_l[rb * 32 + (lane & 31)];
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      float* dst = w.slot < 0 ? a.out + (tree_row0 + r) * mf::DC
+                              : a.ws_o + (w.slot * kMfmaRows + rb * 32 + (lane & 31)) * mf::DC;
+      dst += 128 * wave + 4 * g2;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 v = make_float4(st.o[db][4 * q4] * inv, st.o[db][4 * q4 + 1] * inv, st.o[db][4 * q4 + 2] * inv,
-                                   st.o[db][4 * q4 + 3] * inv);
-      *reinterpret_cast<float4*>(dst + 32 * db + 8 * q4 + 4 * g2) = v;
+      for (int db = 0; db < 4; ++db) {
+        const f32x16_t& v = o[4 * rb + db];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          *reinterpret_cast<float4*>(dst + 32 * db + 8 * q4) =
+              make_float4(v[4 * q4] * inv, v[4 * q4 + 1] * inv, v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv);
+        }
+      }
     }
   }
 }

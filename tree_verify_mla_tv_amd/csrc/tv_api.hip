@@ -33,6 +33,9 @@ tv_status_t check_attn_shape(int32_t prefix_len, int32_t B, int32_t H, int32_t q
   if (prefix_len > INT32_MAX - TV_MAX_Q_LEN) return TV_ERR_INVALID;
   if (static_cast<int64_t>(q_len) * H > (1 << 24)) return TV_ERR_UNSUPPORTED;
   if (!supported_attn(d_c, d_r, kv_dtype)) return TV_ERR_UNSUPPORTED;
+  // The kernels address one tree's latent rows with 32-bit byte offsets.
+  const int64_t elem = kv_dtype == TV_BF16 ? 2 : 4;
+  if ((static_cast<int64_t>(prefix_len) + q_len) * d_c * elem >= (int64_t{1} << 31)) return TV_ERR_UNSUPPORTED;
   return TV_OK;
 }
 
