@@ -28,11 +28,11 @@
 // range once more, with m_ref = the exact row max for the rows that ran out of
 // headroom, so nothing overflows for any finite input.
 //
-// Step t of the sweep (one barrier): the copy of tile t+1 HBM -> LDS starts
-// (global_load_lds_dwordx4, three tile buffers in rotation); scores of tile t
-// (TV_QK_ASM); mask and row max; then one asm block (TV_PVS_ASM) runs the
-// value product of tile t-1 and, woven between its matrix ops, the
-// exponentials, bf16 packing, row sums and LDS stores of tile t's weights.
+// Step t of the sweep is one barrier and one asm block (TV_STEP_ASM): the
+// scores of tile t with the copy of tile t+1 HBM -> LDS woven in (three tile
+// buffers in rotation), then the value product of tile t-1 with the mask, row
+// max, exponentials, bf16 packing, row sums and LDS stores of tile t's weights
+// woven in.
 #include "tv_kernels.h"
 #include "attn_mfma_asm.h"
 
@@ -78,30 +78,57 @@ __shared__ __align__(16) unsigned char g_p[2][mf::kPBytes];
 //                 copies rows 8w .. 8w+7, one wave-wide 1 KB copy per row.
 //   rope rows:    wave w copies keys 8w .. 8w+7 into buf + kLatBytes + 1024 w,
 //                 chunk-major: 16-byte chunk c of key k at slot c * 8 + (k % 8).
-// Buffer loads straight to LDS (buffer_load_dwordx4 ... lds): the tree's base
-// is in the scalar resource, the row in a scalar offset, and each lane adds its
-// 16-byte chunk (lane16 = 16 * lane), so a copy costs no address registers.
-// Nine loads per wave; the caller waits for them (vmcnt) before the barrier
-// that publishes the tile.
+// Buffer loads straight to LDS (buffer_load_dwordx4 ... lds, TV_STAGE_ASM): the
+// tree's base is in a raw buffer descriptor, the row in a scalar offset, and
+// each lane adds its 16-byte chunk.  Nine loads per wave; the caller waits for
+// them (vmcnt) before the barrier that publishes the tile.  Inside the sweep
+// the same loads are woven into the score chain (TV_STEP_ASM).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
 struct TreeKv {
-  __amdgpu_buffer_rsrc_t lat;   // c_kv rows of the tree, 1024 B each
-  __amdgpu_buffer_rsrc_t rope;  // k_rope rows of the tree, 128 B each
+  u32x4_t lat;      // raw buffer over the tree's c_kv rows (1024 B each)
+  u32x4_t rope;     // raw buffer over the tree's k_rope rows (128 B each)
+  uint32_t lane16;  // 16 * lane: the lane's chunk of a latent row
+  int kmax;         // last key of the unit's kv range
 };
 
-__device__ __forceinline__ void stage_tile(unsigned char* buf, const TreeKv& kv, int kt, int k_end, int wave,
-                                           int lane, uint32_t lane16) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int k = wave * 8 + r;
-    const int key = min(kt + k, k_end - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kv.lat, (lds_ptr_t)(buf + k * mf::kLatRowBytes), 16, lane16,
-                                             key * (mf::DC * 2), 0, 0);
-  }
-  const int c = lane >> 3;
-  const int kl = lane & 7;
-  const int key = min(kt + wave * 8 + kl, k_end - 1);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(kv.rope, (lds_ptr_t)(buf + mf::kLatBytes + wave * 1024), 16,
-                                           key * (mf::DR * 2) + c * 16, 0, 0, 0);
+// Raw (untyped) buffer descriptor: base address, stride 0, size in bytes, and
+// dword 3 as for any untyped gfx9 buffer.
+__device__ __forceinline__ u32x4_t raw_buffer(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{static_cast<uint32_t>(p), static_cast<uint32_t>(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Per-tile arguments of a copy into buf of the tile starting at key kt.
+struct StageArgs {
+  uint32_t mb;  // LDS address of the wave's first latent row
+  uint32_t mr;  // LDS address of the wave's rope rows
+  int kb;       // first key of the wave's rows
+  uint32_t ro;  // the lane's rope byte offset in the buffer
+};
+
+__device__ __forceinline__ StageArgs stage_args(const unsigned char* buf, const TreeKv& kv, int kt, int wave,
+                                                int lane) {
+  StageArgs sa;
+  sa.mb = lds_addr(buf) + wave * 8 * mf::kLatRowBytes;
+  sa.mr = lds_addr(buf) + mf::kLatBytes + wave * 1024;
+  sa.kb = kt + wave * 8;
+  sa.ro = static_cast<uint32_t>(min(sa.kb + (lane & 7), kv.kmax)) * (mf::DR * 2) + (lane >> 3) * 16;
+  return sa;
+}
+
+__device__ __forceinline__ void stage_tile(const unsigned char* buf, const TreeKv& kv, int kt, int wave, int lane) {
+  const StageArgs sa = stage_args(buf, kv, kt, wave, lane);
+  const uint32_t mb = __builtin_amdgcn_readfirstlane(sa.mb);
+  const uint32_t mr = __builtin_amdgcn_readfirstlane(sa.mr);
+  const int kb = __builtin_amdgcn_readfirstlane(sa.kb);
+  const int km = __builtin_amdgcn_readfirstlane(kv.kmax);
+  uint32_t t, ms;
+  asm volatile(TV_STAGE_ASM
+               : [t] "=&s"(t), [ms] "=&s"(ms)
+               : [mb] "s"(mb), [mr] "s"(mr), [kb] "s"(kb), [km] "s"(km), [l16] "v"(kv.lane16),
+                 [ro] "v"(sa.ro), [rl] "s"(kv.lat), [rr] "s"(kv.rope)
+               : "memory");
 }
 
 // Per-lane row state of the softmax (rows of the wave's own row block).
@@ -109,107 +136,81 @@ struct RowState {
   float m_ref;   // reference max (log2 units) the exponentials are taken against
   float m_seen;  // exact running max of the row's visible scores (log2 units)
   float l;       // this lane's share of the row's softmax denominator
-  bool over;     // a score exceeded m_ref + kHeadroom
+  float exc;     // largest (tile max - m_ref) seen; above kHeadroom means overflow risk
 };
 
-// Lanes l and l + 32 hold the same row: swap the wave's halves and combine.
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
+// Lanes l and l + 32 hold the same row: swap the wave's halves and add.
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// S^T = K Q^T for one tile (lane: row lane % 32, keys 8 (i/4) + 4 g + i % 4 in
-// register i), masked, and the row's max folded into the state.  Returns the
-// reference the exponentials are taken against.
-__device__ __forceinline__ float scores(const unsigned char* buf, const bf16x8_t* qf, const unsigned char* qrope,
-                                        RowState& st, int lane, int kt, int k_end, int P, unsigned long long anc,
-                                        float (&s)[16]) {
-  const int g2 = lane >> 5;
-  const int key_l = lane & 31;
-  // 36 MFMAs 32x32x16 in one accumulator chain: the latent part of Q is in
-  // registers (qf), the rope part in LDS (qrope, chunk-major); every K
-  // fragment is read 4 MFMAs ahead of its use.
-  const uint32_t lat = lds_addr(buf + key_l * mf::kLatRowBytes + g2 * 16);
-  const uint32_t rope = lds_addr(buf + mf::kLatBytes + (key_l >> 3) * 1024 + (key_l & 7) * 16 + g2 * 128);
-  const uint32_t qr = lds_addr(qrope + g2 * (kMfmaRows * 16));
-  f32x16_t sacc;
-  bf16x8_t k0, k1, k2, k3, k4, k5, r0, r1, r2, r3;
-  asm volatile(TV_QK_ASM
-               : [s] "=&v"(sacc), [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2), [k3] "=&v"(k3), [k4] "=&v"(k4),
-                 [k5] "=&v"(k5), [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3)
-               : [lat] "v"(lat), [rope] "v"(rope), [qr] "v"(qr), [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]),
-                 [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]),
-                 [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),
-                 [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), [q18] "v"(qf[18]),
-                 [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), [q22] "v"(qf[22]), [q23] "v"(qf[23]),
-                 [q24] "v"(qf[24]), [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]),
-                 [q29] "v"(qf[29]), [q30] "v"(qf[30]), [q31] "v"(qf[31])
-               : "memory");
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = sacc[i];
+// Buffers of one step: scores of the tile in kc (keys from kt), values of the
+// tile in kp with the weights pp, this tile's weights to pc, and the copy of
+// the tile after kc into kn.
+struct StepBufs {
+  const unsigned char* kc;
+  const unsigned char* kp;
+  const unsigned char* kn;
+  const unsigned char* pp;
+  unsigned char* pc;
+};
 
-  // Mask (only tiles reaching past the prefix or the unit's kv range).
-  if (kt + kMfmaKeys > P || kt + kMfmaKeys > k_end) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kt + 8 * (i >> 2) + 4 * g2 + (i & 3);
-      const int rel = key - P;  // tree node of a tree row; the bit test is valid for 0 <= rel < 64
-      const bool tree_vis = (static_cast<unsigned>(rel) < 64u) & (((anc >> (rel & 63)) & 1ull) != 0ull);
-      const bool vis = (key < k_end) & ((key < P) | tree_vis);
-      s[i] = vis ? s[i] : -INFINITY;
-    }
-  }
-
-  float mt = s[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
-  mt = max_halves(mt);
-  st.m_seen = fmaxf(st.m_seen, mt);
-  if (st.m_ref == -INFINITY) st.m_ref = mt;  // first visible tile: nothing accumulated yet
-  st.over = st.over || (mt > st.m_ref + mf::kHeadroom);
-  return st.m_ref == -INFINITY ? 0.f : st.m_ref;
-}
-
-// O^T += V^T P^T for the previous tile (kp, weights pp) with this tile's
-// softmax (scores s against mref, weights to pc) woven in.  v_exp_f32 is used
-// directly: its arguments are <= 64 or -inf (masked keys, giving 0), and
-// results below the normal range may flush to 0, which only drops keys
-// weighing < 2^-126 of the reference.
-__device__ __forceinline__ void value_and_softmax(const unsigned char* kp, const unsigned char* pp, unsigned char* pc,
-                                                  f32x16_t (&o)[16], float (&s)[16], float mref, float& l,
-                                                  int lane, int wave) {
+// One step (TV_STEP_ASM): S^T = K Q^T for the tile in kc (lane: row
+// lane % 32, keys 8 (i/4) + 4 g + i % 4 in score i), masked where bit i of
+// vis is clear (if nm), row max folded into the state, weights exp2(s - ref)
+// summed into st.l and stored to pc; O^T += V^T P^T for the previous tile; the
+// copy of the next tile into kn.
+__device__ __forceinline__ void step(const StepBufs& sb, const TreeKv& kv, const bf16x8_t* qf,
+                                     const unsigned char* qrope, f32x16_t (&o)[16], RowState& st, int lane,
+                                     int wave, int kt, uint32_t vis, int nm) {
   const int g2 = lane >> 5;
   const int grp = lane >> 4;
   const int j = lane & 15;
-  // ds_read_b64_tr_b16: in each 16-lane group lane j points at 4 consecutive
-  // latent columns of key row 4 g + j / 4 and receives, for column
-  // 16 (grp & 1) + j, the 4 keys of those rows.
-  const uint32_t tb =
-      lds_addr(kp + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + (16 * (grp & 1) + 4 * (j & 3)) * 2 + 256 * wave);
-  const uint32_t pb = lds_addr(pp + lane * 16);
-  const uint32_t pw0 = lds_addr(pc + wave * 2048 + lane * 16);
-  const uint32_t pw1 = pw0 + 1024;
-  bf16x8_t pi0, pi1, pi2, pi3, pi4, pi5, pi6, pi7;
-  uint32_t pk0, pk1, pk2, pk3, pk4, pk5, pk6, pk7;
-  asm volatile(TV_PVS_ASM
+  const int key_l = lane & 31;
+  // Score fragments: K row key_l, 16 bytes at 32 ks (latent) or chunk-major
+  // rope; query rope fragments chunk-major in qrope.
+  const uint32_t lat = lds_addr(sb.kc + key_l * mf::kLatRowBytes + g2 * 16);
+  const uint32_t rope = lds_addr(sb.kc + mf::kLatBytes + (key_l >> 3) * 1024 + (key_l & 7) * 16 + g2 * 128);
+  const uint32_t qr = lds_addr(qrope + g2 * (kMfmaRows * 16));
+  // Value fragments by ds_read_b64_tr_b16: in each 16-lane group, lane
+  // j = 4 m + q reads 8 bytes (4 consecutive latent columns) of key row
+  // 4 g2 + m, and output lane 4 q + e receives element e of lane 4 m + q's
+  // piece as its key m.  Lane (m, q) of group parity gp = grp & 1 reads the
+  // columns 128 wave + 32 q + 8 db + 4 gp + {0..3} (column set db = 0..3), so
+  // the 32 lanes served together (4 rows, row pitch 1040 B) fall on 32
+  // distinct 8-byte bank slots; the accumulators' columns are permuted the
+  // same way and put back in order when the output is stored.
+  const uint32_t tb = lds_addr(sb.kp + (4 * g2 + (j >> 2)) * mf::kLatRowBytes + 64 * (j & 3) + 8 * (grp & 1) +
+                               256 * wave);
+  const uint32_t pb = lds_addr(sb.pp + lane * 16);
+  const uint32_t pw = lds_addr(sb.pc + wave * 2048 + lane * 16);
+  const StageArgs sa = stage_args(sb.kn, kv, kt + kMfmaKeys, wave, lane);
+  // Scalar operands are wave-uniform by construction; readfirstlane makes
+  // that visible to the compiler, which must place them in SGPRs.
+  const uint32_t mb = __builtin_amdgcn_readfirstlane(sa.mb);
+  const uint32_t mr = __builtin_amdgcn_readfirstlane(sa.mr);
+  const int kb = __builtin_amdgcn_readfirstlane(sa.kb);
+  const int km = __builtin_amdgcn_readfirstlane(kv.kmax);
+  const int nms = __builtin_amdgcn_readfirstlane(nm);
+  uint32_t t, ms;
+  asm volatile(TV_STEP_ASM
                : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]),
                  [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]),
                  [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]),
-                 [o15] "+a"(o[15]), [s0] "+v"(s[0]), [s1] "+v"(s[1]), [s2] "+v"(s[2]), [s3] "+v"(s[3]),
-                 [s4] "+v"(s[4]), [s5] "+v"(s[5]), [s6] "+v"(s[6]), [s7] "+v"(s[7]), [s8] "+v"(s[8]),
-                 [s9] "+v"(s[9]), [s10] "+v"(s[10]), [s11] "+v"(s[11]), [s12] "+v"(s[12]), [s13] "+v"(s[13]),
-                 [s14] "+v"(s[14]), [s15] "+v"(s[15]), [l] "+v"(l), [pi0] "=&v"(pi0), [pi1] "=&v"(pi1),
-                 [pi2] "=&v"(pi2), [pi3] "=&v"(pi3), [pi4] "=&v"(pi4), [pi5] "=&v"(pi5), [pi6] "=&v"(pi6),
-                 [pi7] "=&v"(pi7), [pk0] "=&v"(pk0), [pk1] "=&v"(pk1), [pk2] "=&v"(pk2), [pk3] "=&v"(pk3),
-                 [pk4] "=&v"(pk4), [pk5] "=&v"(pk5), [pk6] "=&v"(pk6), [pk7] "=&v"(pk7)
-               : [mref] "v"(mref), [tb] "v"(tb), [pb] "v"(pb), [pw0] "v"(pw0), [pw1] "v"(pw1)
-               : "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251",
-                 "v252", "v253", "v254", "v255", "memory");
+                 [o15] "+a"(o[15]), [l] "+v"(st.l), [mref] "+v"(st.m_ref), [mseen] "+v"(st.m_seen),
+                 [exc] "+v"(st.exc), [t] "=&s"(t), [ms] "=&s"(ms)
+               : [lat] "v"(lat), [rope] "v"(rope), [qr] "v"(qr), [tb] "v"(tb), [pb] "v"(pb), [pw] "v"(pw),
+                 [mb] "s"(mb), [mr] "s"(mr), [kb] "s"(kb), [km] "s"(km), [l16] "v"(kv.lane16),
+                 [ro] "v"(sa.ro), [rl] "s"(kv.lat), [rr] "s"(kv.rope), [mask] "v"(vis), [nm] "s"(nms),
+                 [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),
+                 [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),
+                 [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]), [q14] "v"(qf[14]),
+                 [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]), [q18] "v"(qf[18]), [q19] "v"(qf[19]),
+                 [q20] "v"(qf[20]), [q21] "v"(qf[21]), [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]),
+                 [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]),
+                 [q30] "v"(qf[30]), [q31] "v"(qf[31])
+               : TV_STEP_CLOBBERS, "vcc", "scc", "memory");
 }
 
 __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArgs a) {
@@ -225,22 +226,17 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   const Unit w = decode_unit(a, unit_of_block(a, blockIdx.x));
   const int b = w.b;
   const int P = a.prefix_len;
-  // Buffer resources over this tree's rows (raw buffers: dword 3 of the
-  // descriptor as for any untyped gfx9 buffer; the host keeps kv_len * 1024
-  // below 2^31, so every offset fits).
+  // Raw buffers over this tree's rows (the host keeps kv_len * 1024 below
+  // 2^31, so every offset fits in 32 bits).
   TreeKv kv;
-  {
-    const uint16_t* ckv_b = static_cast<const uint16_t*>(a.c_kv) + static_cast<int64_t>(b) * a.kv_len * mf::DC;
-    const uint16_t* krope_b = static_cast<const uint16_t*>(a.k_rope) + static_cast<int64_t>(b) * a.kv_len * mf::DR;
-    kv.lat = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ckv_b), 0, a.kv_len * (mf::DC * 2), 0x00020000);
-    kv.rope = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(krope_b), 0, a.kv_len * (mf::DR * 2), 0x00020000);
-  }
-  const uint32_t lane16 = lane * 16;
+  kv.lat = raw_buffer(static_cast<const uint16_t*>(a.c_kv) + static_cast<int64_t>(b) * a.kv_len * mf::DC,
+                      static_cast<uint32_t>(a.kv_len) * (mf::DC * 2));
+  kv.rope = raw_buffer(static_cast<const uint16_t*>(a.k_rope) + static_cast<int64_t>(b) * a.kv_len * mf::DR,
+                       static_cast<uint32_t>(a.kv_len) * (mf::DR * 2));
+  kv.lane16 = lane * 16;
+  kv.kmax = w.k_end - 1;
 
   const int n_tiles = (w.k_end - w.k_begin + kMfmaKeys - 1) / kMfmaKeys;
-  auto stage = [&](unsigned char* buf, int t) {
-    stage_tile(buf, kv, w.k_begin + t * kMfmaKeys, w.k_end, wave, lane, lane16);
-  };
 
   build_ancestors(a.parent + static_cast<int64_t>(b) * a.q_len, a.q_len, s_par, s_anc);
 
@@ -286,7 +282,11 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   }
   const unsigned char* qrope = s_qrope + (wave * 32 + (lane & 31)) * 16;
 
-  f32x16_t o[16];  // o[4 rb + db][i] = O[32 rb + lane % 32][128 wave + 32 db + 8 (i/4) + 4 g2 + i % 4]
+  // o[4 rb + db][i] = O[32 rb + lane % 32][col(db, i)] with (value-operand row
+  // 8 (i/4) + 4 g2 + i % 4 = 16 gp + 4 q + e, see step)
+  //   col(db, i) = 128 wave + 32 q + 8 db + 4 gp + e
+  //              = 128 wave + 64 ((i >> 2) & 1) + 32 g2 + 8 db + 4 (i >> 3) + (i & 3).
+  f32x16_t o[16];
   RowState st;
   st.m_ref = -INFINITY;
   st.m_seen = -INFINITY;
@@ -295,50 +295,66 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = f32x16_t{};
     st.l = 0.f;
-    st.over = false;
+    st.exc = -INFINITY;
     // The weights "before tile 0" are zeros, so step 0's value product adds
     // nothing (it reads tile 0's finite latent rows).
     *reinterpret_cast<uint4*>(g_p[1] + threadIdx.x * 32) = make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(g_p[1] + threadIdx.x * 32 + 16) = make_uint4(0, 0, 0, 0);
-    stage(g_k0, 0);
+    stage_tile(g_k0, kv, w.k_begin, wave, lane);
     unsigned char* kp = g_k2;  // tile t-1
     unsigned char* kc = g_k0;  // tile t
     unsigned char* kn = g_k1;  // tile t+1
-    // Step t: scores of tile t, value product of tile t-1.  The extra step
-    // t = n_tiles only runs the value product of the last tile.
+    // Step t: scores of tile t, value product of tile t-1, copy of tile t+1.
+    // The extra step t = n_tiles has nothing to score (every key masked; its
+    // tile buffer holds the clamped copy made at the step before) and runs
+    // the value product of the last tile.  Copies past the unit's range are
+    // clamped to its last row and land in buffers nobody reads again.
     for (int t = 0; t <= n_tiles; ++t) {
       // Tile t (this wave's copies) has landed; after the barrier every wave's
       // has, the weights of tile t-1 are in LDS, and tile t-2's buffer (kn) and
       // weights buffer are no longer read.  The barrier alone drains only LDS
       // instructions, not the HBM->LDS copies, and the compiler cannot see the
-      // LDS reads inside the asm blocks.
+      // LDS accesses inside the asm blocks.
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (t + 1 < n_tiles) stage(kn, t + 1);
-      float s[16];
-      float mref = 0.f;
-      if (t < n_tiles) {
-        mref = scores(kc, qf, qrope, st, lane, w.k_begin + t * kMfmaKeys, w.k_end, P, anc, s);
-      } else {
+      const int kt = w.k_begin + t * kMfmaKeys;
+      uint32_t vis = 0xffffu;
+      int nm = 0;
+      if (t == n_tiles) {
+        vis = 0;
+        nm = 1;
+      } else if (kt + kMfmaKeys > P || kt + kMfmaKeys > w.k_end) {
+        // Score i holds key kt + 8 (i/4) + 4 g2 + i % 4.
+        nm = 1;
+        vis = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt + 8 * (i >> 2) + 4 * g2 + (i & 3);
+          const int rel = key - P;  // tree node of a tree row; the bit test is valid for 0 <= rel < 64
+          const bool tree_vis = (static_cast<unsigned>(rel) < 64u) & (((anc >> (rel & 63)) & 1ull) != 0ull);
+          const bool v = (key < w.k_end) & ((key < P) | tree_vis);
+          vis |= static_cast<uint32_t>(v) << i;
+        }
       }
-      value_and_softmax(t == 0 ? kc : kp, g_p[(t + 1) & 1], g_p[t & 1], o, s, mref, st.l, lane, wave);
+      const StepBufs sb{kc, t == 0 ? kc : kp, kn, g_p[(t + 1) & 1], g_p[t & 1]};
+      step(sb, kv, qf, qrope, o, st, lane, wave, kt, vis, nm);
       unsigned char* nx = kp;
       kp = kc;
       kc = kn;
       kn = nx;
     }
+    asm volatile("s_waitcnt vmcnt(0)\n" TV_MFMA_DRAIN_ASM ::: "memory");
     // Re-sweep (once, with the exact max as reference) if any row overflowed headroom.
+    const bool over = st.exc > mf::kHeadroom;
     if (threadIdx.x == 0) s_redo = 0;
     __syncthreads();
-    if (__any(st.over) && lane == 0) s_redo = 1;
+    if (__any(over) && lane == 0) s_redo = 1;
     __syncthreads();
     if (pass > 0 || s_redo == 0) break;
     // Only rows that ran out of headroom move their reference, so every other
     // row repeats its first sweep bit for bit (a row's result never depends on
     // another row's scores).
-    st.m_ref = st.over ? st.m_seen : st.m_ref;
+    st.m_ref = over ? st.m_seen : st.m_ref;
   }
 
   // Row sums of the wave's own rows, for all four waves.
@@ -364,13 +380,13 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
       float* dst = w.slot < 0 ? a.out + (tree_row0 + r) * mf::DC
                               : a.ws_o + (w.slot * kMfmaRows + rb * 32 + (lane & 31)) * mf::DC;
-      dst += 128 * wave + 4 * g2;
+      dst += 128 * wave + 32 * g2;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const f32x16_t& v = o[4 * rb + db];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          *reinterpret_cast<float4*>(dst + 32 * db + 8 * q4) =
+          *reinterpret_cast<float4*>(dst + 64 * (q4 & 1) + 8 * db + 4 * (q4 >> 1)) =
               make_float4(v[4 * q4] * inv, v[4 * q4 + 1] * inv, v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv);
         }
       }

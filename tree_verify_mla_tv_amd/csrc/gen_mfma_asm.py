@@ -1,52 +1,90 @@
 #!/usr/bin/env python3
-"""Generate attn_mfma_asm.h: the two inline-asm blocks of attn_mfma.hip.
+"""Generate attn_mfma_asm.h: the inline-asm blocks of attn_mfma.hip.
 
     python tree_verify_mla_tv_amd/csrc/gen_mfma_asm.py   # rewrites attn_mfma_asm.h
 
-The blocks are written out instruction by instruction so that every LDS read
-is issued well ahead of the matrix op that consumes it and the softmax VALU
-work sits between matrix ops (the compiler, short of registers next to 256
-accumulators and 128 query registers, otherwise places each read right before
-its consumer, waits for it, and runs the softmax between the two products).
-Register choice stays with the compiler through named operands, except for the
-four value-fragment slots (see below); only order and waits are fixed here.
+One step of the kv sweep is one asm block, written out instruction by
+instruction, so that the matrix core never waits on anything the schedule can
+hide: every LDS fragment is read several matrix ops ahead of its use, the
+value product of the previous tile starts right behind the last score op, and
+the mask, row max and softmax of this tile run between value ops.  (Left to
+the compiler, short of registers next to 256 accumulators and 128 query
+registers, each read lands right before its consumer and the VALU work runs
+between the two products.)
 
-TV_QK_ASM -- scores of one tile, per wave: 36 x v_mfma_f32_32x32x16_bf16 into
-  %[s].  k-step ks < 32 reads its K fragment at %[lat] + 32 ks, ks >= 32 at
-  %[rope] + 256 (ks - 32); its Q fragment is %[qN] for ks < 32, and for
-  ks >= 32 an LDS fragment at %[qr] + 4096 (ks - 32), read first into %[rN].
+TV_STEP_ASM -- per wave, for tile t (scores) and tile t-1 (values):
+  1. Scores S^T = K Q^T: 36 x v_mfma_f32_32x32x16_bf16 into S (v[176:191]).
+     k-step ks < 32 takes its K fragment at %[lat] + 32 ks and the query
+     fragment %[q<ks>]; ks >= 32 takes K at %[rope] + 256 (ks - 32) and the
+     query fragment at %[qr] + 4096 (ks - 32) (rope part, LDS).
+     Woven in: this wave's copy of tile t+1 (the TV_STAGE_ASM loads, one every
+     second op), so that the four waves never queue 36 LDS-DMA loads at once.
+  2. Values O^T[rb][db] (%[o<4 rb + db>]) += V(db, h) x P(rb, h) for tile t-1:
+     32 MFMAs, n = 16 h + 4 db + rb.  V(db, h) is read from the row-major tile
+     with two ds_read_b64_tr_b16 at %[tb] + 16640 h + 16 db (+ 8320 for keys
+     8..15 of the half); P(rb, h), tile t-1's bf16 weights, with ds_read_b128
+     at %[pb] + 1024 (2 rb + h).
+     Woven in, for tile t (all VALU, lane = one query row, 16 of its scores):
+       mask   (only when %[nm] != 0): score i becomes -inf unless bit i of
+              %[mask] is set;
+       max    over the 16 scores and the other half of the wave (the lane
+              l ^ 32 holds the same row: v_permlane32_swap);
+       state  %[mseen] = max(%[mseen], max); %[mref] takes the max if it was
+              -inf (first visible tile); %[exc] = max(%[exc], max - %[mref]);
+              the reference used is max(%[mref], -FLT_MAX) (equal to %[mref]
+              unless every score so far is -inf, when exp2(-inf - ref) = 0);
+       weights  s <- exp2(s - ref), packed to bf16 pairs in v[240:247], summed
+              into %[l] with bf16 dot products against (1, 1) (two partial
+              chains), and stored with ds_write_b128 at %[pw] (keys 0..15)
+              and %[pw] + 1024.
+     These ops form a dependency graph that is list-scheduled into the gaps
+     between value ops, at most VALU_PER_GAP per gap, never in the same gap
+     as an op whose result they read: with one wave per SIMD, issue is in
+     order, and a dependent op right behind its producer would hold back the
+     next matrix op.
+All LDS fragments go through a pool of register quads v[192:239] assigned here
+(an MFMA operand must be one register quad, and an asm operand cannot be
+split); a quad is reused one matrix op after its last reader.  Waits are
+exact lgkmcnt counts from a simulation of the wave's in-order LDS queue.
 
-TV_PVS_ASM -- value product of the previous tile with this tile's softmax woven
-  in.  Value part: 32 MFMAs, n = 16 h + 4 db + rb, accumulate
-  O[rb][db] (%[o<4 rb + db>]) += V(db, h) x P(rb, h), where
-    V(db, h)  this wave's d-block db (32 latent columns) of key half h, read
-              from the row-major tile with two ds_read_b64_tr_b16 at
-              %[tb] + 16640 h + 64 db (+ 8320 for keys 8..15 of the half) into
-              one of four fixed register quads v[240:255] (an MFMA operand
-              must be one quad, and an operand of the asm cannot be split);
-    P(rb, h)  the previous tile's bf16 weights of row block rb, key half h,
-              read with ds_read_b128 at %[pb] + 1024 (2 rb + h) into %[pi<2 rb + h>].
-  Softmax part: for this tile's 16 scores %[s0..15] of the lane's row,
-  s <- exp2(s - %[mref]), packed to bf16 pairs %[pk0..7], summed into %[l]
-  with a bf16 dot product against (1, 1), and stored at %[pw0] (keys of half 0)
-  and %[pw1] (half 1).
+TV_STAGE_ASM -- the copy alone: wave w's nine buffer_load_dwordx4 ... lds of a
+  tile.  Latent row r = 0..7 (key min(%[kb] + r, %[km])) lands at LDS
+  %[mb] + 1040 r from buffer %[rl] at byte key * 1024 + %[l16]; the rope rows
+  land at %[mr] from buffer %[rr] at per-lane byte %[ro].  M0 (the LDS
+  destination of a DMA load) is saved in %[ms] and restored at the end, and
+  %[t] holds each row's buffer offset.
 
-Hazards handled inside the blocks: LDS data waits (s_waitcnt lgkmcnt, counted
-by simulating the in-order LDS queue of the block's own reads and writes),
-the distance between a transcendental result and its first use, and the
-matrix-core results before anything outside a block reads them (s_nop padding
-at the end of each block).
+Hazards handled inside the blocks: LDS data waits; the matrix-core result S
+before the first VALU read (>= 19 wait states); the M0 and offset writes a
+matrix op before the DMA load that reads them; v_permlane32_swap two wait
+states after the VALU write of its operand; every transcendental result used
+a matrix op or more later; the accumulators before anything outside the
+sweep reads them (TV_MFMA_DRAIN_ASM after the last step).
 """
 import os
 
-DEPTH = 4   # score chain: K reads in flight ahead of the matrix op that consumes them
-SLOTS = 6   # score chain: rotating K fragment registers
+S_BASE = 176                                  # v[176:191]: the 16 scores (MFMA accumulator)
+POOL = [192 + 4 * i for i in range(12)]       # v[192:239]: LDS fragment quads
+P_QUADS = [240, 244]                          # v[240:247]: packed weights, key half 0 and 1
+TMP = [248, 249, 250, 251, 252]               # v[248:252]: VALU temporaries
+CLOBBERED = list(range(S_BASE, 253))
+AHEAD = 6        # a fragment is read at most this many matrix ops before its first use
+QK_COPY_GROUPS = 18   # copy groups issued among the score ops; the rest go among the value ops
+VALU_PER_GAP = 3      # softmax ops between two value ops
 NOP_AFTER = "s_nop 7\\n s_nop 7\\n s_nop 7\\n"   # >= 19 wait states after the last MFMA
-V_QUADS = [240, 244, 248, 252]   # value-fragment register quads of TV_PVS_ASM
-V_AHEAD = 2                      # value fragments loaded ahead of the one in use
+NEG_INF = "0xff800000"
+ONE_ONE_BF16 = "0x3f803f80"
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(HERE, "attn_mfma_asm.h")
+
+
+def S(i):
+    return f"v{S_BASE + i}"
+
+
+def quad(r):
+    return f"v[{r}:{r + 3}]"
 
 
 class LdsQueue:
@@ -66,118 +104,229 @@ class LdsQueue:
         self.lines.append(f"s_waitcnt lgkmcnt({min(len(self.issued) - idx - 1, 15)})")
 
 
-def qk_asm() -> str:
-    lines = []
-    q = LdsQueue(lines)
-    for r in range(4):
-        q.issue(f"ds_read_b128 %[r{r}], %[qr] offset:{4096 * r}", f"r{r}")
-
-    def k_read(ks):
-        slot = ks % SLOTS
-        if ks < 32:
-            q.issue(f"ds_read_b128 %[k{slot}], %[lat] offset:{32 * ks}", f"k{ks}")
-        else:
-            q.issue(f"ds_read_b128 %[k{slot}], %[rope] offset:{256 * (ks - 32)}", f"k{ks}")
-
-    for ks in range(DEPTH):
-        k_read(ks)
-    for ks in range(36):
-        if ks < 32:
-            q.wait_for(f"k{ks}")
-            src_b = f"%[q{ks}]"
-        else:
-            q.wait_for(f"k{ks}", f"r{ks - 32}")
-            src_b = f"%[r{ks - 32}]"
-        src_c = "0" if ks == 0 else "%[s]"
-        lines.append(f"v_mfma_f32_32x32x16_bf16 %[s], %[k{ks % SLOTS}], {src_b}, {src_c}")
-        if ks + DEPTH < 36:
-            k_read(ks + DEPTH)
-    return "\\n".join(lines) + "\\n" + NOP_AFTER
+def stage_ops():
+    """The tile copy as groups of instructions; a group is issued after one
+    matrix op.  The address group of a row and its load sit one op apart, so
+    the M0 / offset writes are a few wait states before the load reads them."""
+    groups = []
+    for r in range(8):
+        m0 = "s_mov_b32 m0, %[mb]" if r == 0 else f"s_add_u32 m0, %[mb], {1040 * r}"
+        groups.append([m0, f"s_add_i32 %[t], %[kb], {r}", "s_min_i32 %[t], %[t], %[km]",
+                       "s_lshl_b32 %[t], %[t], 10"])
+        groups.append(["buffer_load_dwordx4 %[l16], %[rl], %[t] offen lds"])
+    groups.append(["s_mov_b32 m0, %[mr]"])
+    groups.append(["buffer_load_dwordx4 %[ro], %[rr], 0 offen lds"])
+    return groups
 
 
-def softmax_ops():
-    """The softmax VALU/LDS work in dependency order, as (text, lds_name or None)."""
+def stage_asm() -> str:
+    lines = ["s_mov_b32 %[ms], m0"]
+    for g in stage_ops():
+        lines.extend(g)
+        lines.append("s_nop 1")
+    lines.append("s_mov_b32 m0, %[ms]")
+    return "\\n".join(lines) + "\\n"
+
+
+def softmax_valu():
+    """Tile t's VALU work as a dependency graph: list of (text, lds_name or
+    None, deps) with deps the indices of earlier ops whose results it reads.
+    The mask is separate (a branch, before all of this)."""
+    t = [f"v{r}" for r in TMP]
     ops = []
+
+    def op(text, deps=(), lds=None):
+        ops.append((text, lds, tuple(deps)))
+        return len(ops) - 1
+
+    # VCC = (m_ref == -inf), taken before m_ref changes.
+    c_ref = op(f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]")
+    # Row max: a tree of v_max3 over the 16 scores, then the other half-wave.
+    a = [op(f"v_max3_f32 {t[k]}, {S(3 * k)}, {S(3 * k + 1)}, {S(3 * k + 2)}") for k in range(5)]
+    b0 = op(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {t[2]}", a[0:3])
+    b1 = op(f"v_max3_f32 {t[3]}, {t[3]}, {t[4]}, {S(15)}", a[3:5])
+    mt = op(f"v_max_f32 {t[0]}, {t[0]}, {t[3]}", [b0, b1])
+    cp = op(f"v_mov_b32 {t[1]}, {t[0]}", [mt])
+    sw = op(f"v_permlane32_swap_b32 {t[0]}, {t[1]}", [cp])
+    mx = op(f"v_max_f32 {t[0]}, {t[0]}, {t[1]}", [sw])
+    # Row state.  m_ref takes the max on the first visible tile; the
+    # reference of this tile's exponentials is max(m_ref, -FLT_MAX): it equals
+    # m_ref unless every score so far is -inf, and then exp2(-inf - ref) = 0.
+    op(f"v_max_f32 %[mseen], %[mseen], {t[0]}", [mx])
+    nr = op(f"v_cndmask_b32 %[mref], %[mref], {t[0]}, vcc", [mx, c_ref])
+    ex = op(f"v_sub_f32 {t[2]}, {t[0]}, %[mref]", [nr])
+    op(f"v_max_f32 %[exc], %[exc], {t[2]}", [ex])
+    ref = op(f"v_max_f32 {t[3]}, 0xff7fffff, %[mref]", [nr])
+    # Weights: s <- exp2(s - ref), packed pairs, two partial sums, stores.
+    ex_of = []
     for i in range(16):
-        ops.append((f"v_sub_f32 %[s{i}], %[s{i}], %[mref]", None))
-        ops.append((f"v_exp_f32 %[s{i}], %[s{i}]", None))
-    for k in range(8):
-        ops.append((f"v_cvt_pk_bf16_f32 %[pk{k}], %[s{2 * k}], %[s{2 * k + 1}]", None))
-        if k >= 1:
-            ops.append((f"v_dot2c_f32_bf16 %[l], 0x3f803f80, %[pk{k - 1}]", None))
-    ops.append(("v_dot2c_f32_bf16 %[l], 0x3f803f80, %[pk7]", None))
+        sb = op(f"v_sub_f32 {S(i)}, {S(i)}, {t[3]}", [ref])
+        ex_of.append(op(f"v_exp_f32 {S(i)}, {S(i)}", [sb]))
+
+    def pk(k):  # packed pair k: scores 2k, 2k+1 (key half k // 4)
+        return f"v{P_QUADS[k // 4] + k % 4}"
+
+    cv = [op(f"v_cvt_pk_bf16_f32 {pk(k)}, {S(2 * k)}, {S(2 * k + 1)}", [ex_of[2 * k], ex_of[2 * k + 1]])
+          for k in range(8)]
+    # Two accumulation chains: even pairs into l, odd pairs into t[4].
+    la = None
+    for k in range(0, 8, 2):
+        la = op(f"v_dot2c_f32_bf16 %[l], {ONE_ONE_BF16}, {pk(k)}", [cv[k]] + ([la] if la is not None else []))
+    lb = op(f"v_mov_b32 {t[4]}, 0")   # (gfx9 VOP3 takes no literal: start the chain at 0)
+    for k in range(1, 8, 2):
+        lb = op(f"v_dot2c_f32_bf16 {t[4]}, {ONE_ONE_BF16}, {pk(k)}", [cv[k], lb])
+    op(f"v_add_f32 %[l], %[l], {t[4]}", [la, lb])
     for h in range(2):
-        for pair in range(2):
-            a, b = 4 * h + 2 * pair, 4 * h + 2 * pair + 1
-            ops.append((f"ds_write2_b32 %[pw{h}], %[pk{a}], %[pk{b}] offset0:{2 * pair} offset1:{2 * pair + 1}",
-                        f"w{h}{pair}"))
+        op(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", cv[4 * h:4 * h + 4], lds=f"w{h}")
     return ops
 
 
-def pvs_asm() -> str:
-    lines = []
-    q = LdsQueue(lines)
+def schedule_valu(ops, n_slots, first_slot, per_slot):
+    """Greedy list schedule of the VALU graph into the gaps after matrix ops:
+    at most per_slot ops per gap, and an op never shares a gap with an op it
+    reads (a matrix op, >= 32 cycles, sits between producer and consumer)."""
+    slot_of = {}
+    out = [[] for _ in range(n_slots)]
+    pending = list(range(len(ops)))
+    for sl in range(first_slot, n_slots):
+        placed = 0
+        for i in list(pending):
+            if placed == per_slot:
+                break
+            if all(d in slot_of and slot_of[d] < sl for d in ops[i][2]):
+                slot_of[i] = sl
+                out[sl].append(ops[i])
+                pending.remove(i)
+                placed += 1
+        if not pending:
+            break
+    assert not pending, "softmax does not fit between the value ops"
+    return out
 
-    def quad(f):
-        return V_QUADS[f % len(V_QUADS)]
 
-    def v_read(f):
-        h, db = f >> 2, f & 3
-        r = quad(f)
-        off = 16640 * h + 64 * db
-        q.issue(f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[tb] offset:{off}", f"vlo{f}")
-        q.issue(f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[tb] offset:{off + 8320}", f"vhi{f}")
+def mask_block():
+    # -inf in a register: v_cndmask with VCC has no constant-bus slot left
+    # for a literal.
+    t0, t1 = f"v{TMP[0]}", f"v{TMP[1]}"
+    lines = ["s_cmp_eq_u32 %[nm], 0", "s_cbranch_scc1 .Ltv_nomask_%=", f"v_mov_b32 {t0}, {NEG_INF}"]
+    for i in range(16):
+        lines += [f"v_bfe_u32 {t1}, %[mask], {i}, 1", f"v_cmp_ne_u32 vcc, 0, {t1}",
+                  f"v_cndmask_b32 {S(i)}, {t0}, {S(i)}, vcc"]
+    lines.append(".Ltv_nomask_%=:")
+    return lines
 
-    def p_read(rb, h):
-        q.issue(f"ds_read_b128 %[pi{2 * rb + h}], %[pb] offset:{1024 * (2 * rb + h)}", f"p{rb}{h}")
 
-    # Weights of key half 0, the first value fragments, then weights of half 1.
-    for rb in range(4):
-        p_read(rb, 0)
-    for f in range(V_AHEAD):
-        v_read(f)
-    for rb in range(4):
-        p_read(rb, 1)
-
-    # Spread the softmax over the 32 matrix ops: two per op while exponentials
-    # remain (they are quarter-rate), then the packing, sums and stores.
-    sm = softmax_ops()
-    per_slot, i = [], 0
+def step_asm() -> str:
+    # Matrix ops in issue order and the fragments each reads.
+    mfma, needs = [], []
+    for ks in range(36):
+        mfma.append(("qk", ks))
+        needs.append([f"K{ks}"] if ks < 32 else [f"K{ks}", f"R{ks - 32}"])
     for n in range(32):
-        take = 2 if n < 24 else 1
-        per_slot.append(sm[i:i + take])
-        i += take
-    per_slot[-1].extend(sm[i:])
+        f, rb = n >> 2, n & 3
+        mfma.append(("pv", n))
+        needs.append([f"V{f}", f"P{rb}{f >> 2}"])
+    first_use, last_use, order = {}, {}, []
+    for m, frs in enumerate(needs):
+        for fr in frs:
+            if fr not in first_use:
+                first_use[fr] = m
+                order.append(fr)
+            last_use[fr] = m
+    # A quad whose last reader is op m goes back to the pool once op m + 1 has
+    # been issued (release[m + 2] is handed back before op m + 2).
+    release = {}
+    for fr, m in last_use.items():
+        release.setdefault(m + 2, []).append(fr)
 
-    for f in range(8):
-        h, db = f >> 2, f & 3
-        r = quad(f)
-        for rb in range(4):
-            n = 4 * f + rb
-            q.wait_for(f"vhi{f}", f"p{rb}{h}")
-            lines.append(f"v_mfma_f32_32x32x16_bf16 %[o{4 * rb + db}], v[{r}:{r + 3}], %[pi{2 * rb + h}], "
-                         f"%[o{4 * rb + db}]")
-            if rb == 0 and f + V_AHEAD < 8:
-                v_read(f + V_AHEAD)
-            for text, lds_name in per_slot[n]:
+    lines = ["s_mov_b32 %[ms], m0"]
+    q = LdsQueue(lines)
+    free = list(POOL)
+    where = {}
+
+    def load(fr):
+        r = free.pop(0)
+        where[fr] = r
+        kind, idx = fr[0], fr[1:]
+        if kind == "K":
+            ks = int(idx)
+            src = f"%[lat] offset:{32 * ks}" if ks < 32 else f"%[rope] offset:{256 * (ks - 32)}"
+            q.issue(f"ds_read_b128 {quad(r)}, {src}", fr)
+        elif kind == "R":
+            q.issue(f"ds_read_b128 {quad(r)}, %[qr] offset:{4096 * int(idx)}", fr)
+        elif kind == "V":
+            f = int(idx)
+            off = 16640 * (f >> 2) + 16 * (f & 3)
+            q.issue(f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[tb] offset:{off}", fr + "lo")
+            q.issue(f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[tb] offset:{off + 8320}", fr)
+        else:  # P<rb><h>
+            rb, h = int(idx[0]), int(idx[1])
+            q.issue(f"ds_read_b128 {quad(r)}, %[pb] offset:{1024 * (2 * rb + h)}", fr)
+
+    stage = stage_ops()
+    stage_qk, stage_pv = stage[:QK_COPY_GROUPS], stage[QK_COPY_GROUPS:]
+    valu = softmax_valu()
+    # VALU work between value ops: the S hazard padding and the (optional)
+    # mask after the first one, then the dependency graph, list-scheduled.
+    n_pv = 32
+    per_op = schedule_valu(valu, n_pv, 1, VALU_PER_GAP)
+
+    nxt = 0
+    for m, (kind, idx) in enumerate(mfma):
+        for fr in release.get(m, []):
+            free.append(where[fr])
+        while nxt < len(order) and first_use[order[nxt]] <= m + AHEAD and free:
+            load(order[nxt])
+            nxt += 1
+        q.wait_for(*needs[m])
+        if kind == "qk":
+            ks = idx
+            a = quad(where[f"K{ks}"])
+            b = f"%[q{ks}]" if ks < 32 else quad(where[f"R{ks - 32}"])
+            c = "0" if ks == 0 else f"v[{S_BASE}:{S_BASE + 15}]"
+            lines.append(f"v_mfma_f32_32x32x16_bf16 v[{S_BASE}:{S_BASE + 15}], {a}, {b}, {c}")
+            if ks < len(stage_qk):
+                lines.extend(stage_qk[ks])
+        else:
+            n = idx
+            f, rb = n >> 2, n & 3
+            o = f"%[o{4 * rb + (f & 3)}]"
+            lines.append(f"v_mfma_f32_32x32x16_bf16 {o}, {quad(where[f'V{f}'])}, "
+                         f"{quad(where[f'P{rb}{f >> 2}'])}, {o}")
+            if n == 0:
+                # The last score op wrote S one value op ago: >= 19 wait
+                # states before the first VALU read of S.
+                lines.append("s_nop 7\\n s_nop 7\\n s_nop 4")
+                lines.extend(mask_block())
+            if n < len(stage_pv):
+                lines.extend(stage_pv[n])
+            for text, lds_name, _ in per_op[n]:
                 if lds_name:
                     q.issue(text, lds_name)
                 else:
                     lines.append(text)
+    assert nxt == len(order)
+    lines.append("s_mov_b32 m0, %[ms]")
     lines.append("s_waitcnt lgkmcnt(0)")
-    return "\\n".join(lines) + "\\n" + NOP_AFTER
+    # No padding: nothing reads the accumulators until after the sweep (the
+    # kernel pads once there, TV_MFMA_DRAIN_ASM).
+    return "\\n".join(lines) + "\\n"
 
 
 def main():
-    qk = qk_asm()
-    pvs = pvs_asm()
     text = f"""// Generated by gen_mfma_asm.py -- do not edit by hand.
 // Inline-asm blocks of attn_mfma.hip (see the generator's docstring).
 #pragma once
 
-#define TV_QK_ASM "{qk}"
+#define TV_STAGE_ASM "{stage_asm()}"
 
-#define TV_PVS_ASM "{pvs}"
+#define TV_STEP_ASM "{step_asm()}"
+
+// After the last step: >= 19 wait states before the accumulators are read.
+#define TV_MFMA_DRAIN_ASM "{NOP_AFTER}"
+
+// Registers the step block uses by number (clobbered).
+#define TV_STEP_CLOBBERS {", ".join(f'"v{r}"' for r in CLOBBERED)}
 """
     with open(OUT, "w") as f:
         f.write(text)

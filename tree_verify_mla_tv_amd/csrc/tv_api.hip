@@ -2,7 +2,7 @@
 // planning and kernel dispatch.  Nothing here allocates or synchronises.
 #include <math.h>
 
-#include "../../include/tv.h"
+#include "tv.h"
 #include "tv_kernels.h"
 
 namespace {
