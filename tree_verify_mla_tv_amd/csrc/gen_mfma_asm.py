@@ -62,15 +62,17 @@ a matrix op or more later; the accumulators before anything outside the
 sweep reads them (TV_MFMA_DRAIN_ASM after the last step).
 """
 import os
+import re
 
 S_BASE = 176                                  # v[176:191]: the 16 scores (MFMA accumulator)
 POOL = [192 + 4 * i for i in range(12)]       # v[192:239]: LDS fragment quads
 P_QUADS = [240, 244]                          # v[240:247]: packed weights, key half 0 and 1
-TMP = [248, 249, 250, 251, 252]               # v[248:252]: VALU temporaries
-CLOBBERED = list(range(S_BASE, 253))
+TMP = list(range(248, 256))                   # v[248:255]: VALU temporaries
+CLOBBERED = list(range(S_BASE, 256))
 AHEAD = 6        # a fragment is read at most this many matrix ops before its first use
 QK_COPY_GROUPS = 18   # copy groups issued among the score ops; the rest go among the value ops
-VALU_PER_GAP = 3      # softmax ops between two value ops
+VALU_PER_GAP = 4      # softmax ops between two value ops
+STORES_AT_END = False # weights stored after the last value op instead of between them
 NOP_AFTER = "s_nop 7\\n s_nop 7\\n s_nop 7\\n"   # >= 19 wait states after the last MFMA
 NEG_INF = "0xff800000"
 ONE_ONE_BF16 = "0x3f803f80"
@@ -128,56 +130,109 @@ def stage_asm() -> str:
     return "\\n".join(lines) + "\\n"
 
 
+def _regs(tok):
+    """Registers named by one operand token: v12, v[12:15], %[name], vcc."""
+    tok = tok.strip()
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return [f"v{r}" for r in range(int(m.group(1)), int(m.group(2)) + 1)]
+    if re.fullmatch(r"v\d+", tok) or tok.startswith("%[") or tok == "vcc":
+        return [tok]
+    return []
+
+
+def _reads_writes(text):
+    mnem, _, rest = text.partition(" ")
+    ops = [o for o in rest.split(",")]
+    ops = [o.split(" offset")[0] for o in ops]
+    regs = [_regs(o) for o in ops]
+    if mnem.startswith("v_cmp"):
+        return sum(regs[1:], []), ["vcc"]
+    if mnem.startswith("v_cndmask"):
+        return sum(regs[1:], []), regs[0]
+    if mnem.startswith("v_permlane32_swap"):
+        return regs[0] + regs[1], regs[0] + regs[1]
+    if mnem.startswith("ds_write"):
+        return sum(regs, []), []
+    if mnem.startswith("v_"):
+        return sum(regs[1:], []), regs[0]
+    return [], []
+
+
 def softmax_valu():
-    """Tile t's VALU work as a dependency graph: list of (text, lds_name or
-    None, deps) with deps the indices of earlier ops whose results it reads.
-    The mask is separate (a branch, before all of this)."""
+    """Tile t's VALU work in program order: list of (text, lds_name or None,
+    deps), deps being the earlier ops this one must follow (it reads their
+    results, or overwrites a register they read or write).  The mask is
+    separate (a branch, before all of this)."""
     t = [f"v{r}" for r in TMP]
     ops = []
+    last_w, last_r = {}, {}
 
-    def op(text, deps=(), lds=None):
-        ops.append((text, lds, tuple(deps)))
-        return len(ops) - 1
+    def op(text, lds=None):
+        rd, wr = _reads_writes(text)
+        deps = set()
+        for r in rd:
+            if r in last_w:
+                deps.add(last_w[r])
+        for r in wr:
+            deps.update(last_r.get(r, ()))
+            if r in last_w:
+                deps.add(last_w[r])
+        i = len(ops)
+        ops.append((text, lds, tuple(sorted(deps))))
+        for r in rd:
+            last_r.setdefault(r, set()).add(i)
+        for r in wr:
+            last_w[r] = i
+            last_r[r] = set()
+        return i
 
     # VCC = (m_ref == -inf), taken before m_ref changes.
-    c_ref = op(f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]")
+    op(f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]")
     # Row max: a tree of v_max3 over the 16 scores, then the other half-wave.
-    a = [op(f"v_max3_f32 {t[k]}, {S(3 * k)}, {S(3 * k + 1)}, {S(3 * k + 2)}") for k in range(5)]
-    b0 = op(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {t[2]}", a[0:3])
-    b1 = op(f"v_max3_f32 {t[3]}, {t[3]}, {t[4]}, {S(15)}", a[3:5])
-    mt = op(f"v_max_f32 {t[0]}, {t[0]}, {t[3]}", [b0, b1])
-    cp = op(f"v_mov_b32 {t[1]}, {t[0]}", [mt])
-    sw = op(f"v_permlane32_swap_b32 {t[0]}, {t[1]}", [cp])
-    mx = op(f"v_max_f32 {t[0]}, {t[0]}, {t[1]}", [sw])
+    for k in range(5):
+        op(f"v_max3_f32 {t[k]}, {S(3 * k)}, {S(3 * k + 1)}, {S(3 * k + 2)}")
+    op(f"v_max3_f32 {t[0]}, {t[0]}, {t[1]}, {t[2]}")
+    op(f"v_max3_f32 {t[3]}, {t[3]}, {t[4]}, {S(15)}")
+    op(f"v_max_f32 {t[0]}, {t[0]}, {t[3]}")
+    op(f"v_mov_b32 {t[1]}, {t[0]}")
+    op(f"v_permlane32_swap_b32 {t[0]}, {t[1]}")
+    op(f"v_max_f32 {t[0]}, {t[0]}, {t[1]}")
     # Row state.  m_ref takes the max on the first visible tile; the
     # reference of this tile's exponentials is max(m_ref, -FLT_MAX): it equals
     # m_ref unless every score so far is -inf, and then exp2(-inf - ref) = 0.
-    op(f"v_max_f32 %[mseen], %[mseen], {t[0]}", [mx])
-    nr = op(f"v_cndmask_b32 %[mref], %[mref], {t[0]}, vcc", [mx, c_ref])
-    ex = op(f"v_sub_f32 {t[2]}, {t[0]}, %[mref]", [nr])
-    op(f"v_max_f32 %[exc], %[exc], {t[2]}", [ex])
-    ref = op(f"v_max_f32 {t[3]}, 0xff7fffff, %[mref]", [nr])
-    # Weights: s <- exp2(s - ref), packed pairs, two partial sums, stores.
-    ex_of = []
+    op(f"v_max_f32 %[mseen], %[mseen], {t[0]}")
+    op(f"v_cndmask_b32 %[mref], %[mref], {t[0]}, vcc")
+    op(f"v_sub_f32 {t[2]}, {t[0]}, %[mref]")
+    op(f"v_max_f32 %[exc], %[exc], {t[2]}")
+    op(f"v_max_f32 {t[3]}, 0xff7fffff, %[mref]")
+    # Weights: s <- exp2(s - ref), packed pairs.
     for i in range(16):
-        sb = op(f"v_sub_f32 {S(i)}, {S(i)}, {t[3]}", [ref])
-        ex_of.append(op(f"v_exp_f32 {S(i)}, {S(i)}", [sb]))
+        op(f"v_sub_f32 {S(i)}, {S(i)}, {t[3]}")
+        op(f"v_exp_f32 {S(i)}, {S(i)}")
 
     def pk(k):  # packed pair k: scores 2k, 2k+1 (key half k // 4)
         return f"v{P_QUADS[k // 4] + k % 4}"
 
-    cv = [op(f"v_cvt_pk_bf16_f32 {pk(k)}, {S(2 * k)}, {S(2 * k + 1)}", [ex_of[2 * k], ex_of[2 * k + 1]])
-          for k in range(8)]
-    # Two accumulation chains: even pairs into l, odd pairs into t[4].
-    la = None
-    for k in range(0, 8, 2):
-        la = op(f"v_dot2c_f32_bf16 %[l], {ONE_ONE_BF16}, {pk(k)}", [cv[k]] + ([la] if la is not None else []))
-    lb = op(f"v_mov_b32 {t[4]}, 0")   # (gfx9 VOP3 takes no literal: start the chain at 0)
-    for k in range(1, 8, 2):
-        lb = op(f"v_dot2c_f32_bf16 {t[4]}, {ONE_ONE_BF16}, {pk(k)}", [cv[k], lb])
-    op(f"v_add_f32 %[l], %[l], {t[4]}", [la, lb])
-    for h in range(2):
-        op(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", cv[4 * h:4 * h + 4], lds=f"w{h}")
+    for k in range(8):
+        op(f"v_cvt_pk_bf16_f32 {pk(k)}, {S(2 * k)}, {S(2 * k + 1)}")
+    # The row sum takes the rounded weights the value product uses: a bf16
+    # value is its bits in the top half of an fp32 word, so each packed pair
+    # unpacks with one shift and one mask, then plain fp32 adds in two chains
+    # (even pairs into l, odd pairs into t[4]).  (v_dot2c_f32_bf16 would add
+    # two at once but holds back the next matrix op by ~16 cycles.)
+    op(f"v_mov_b32 {t[4]}, 0")
+    for k in range(8):
+        acc = "%[l]" if k % 2 == 0 else t[4]
+        lo, hi = (t[5], t[6]) if k % 2 == 0 else (t[7], t[1])
+        op(f"v_lshlrev_b32 {lo}, 16, {pk(k)}")
+        op(f"v_and_b32 {hi}, 0xffff0000, {pk(k)}")
+        op(f"v_add_f32 {acc}, {acc}, {lo}")
+        op(f"v_add_f32 {acc}, {acc}, {hi}")
+    op(f"v_add_f32 %[l], %[l], {t[4]}")
+    if not STORES_AT_END:
+        for h in range(2):
+            op(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", lds=f"w{h}")
     return ops
 
 
@@ -306,6 +361,9 @@ def step_asm() -> str:
                 else:
                     lines.append(text)
     assert nxt == len(order)
+    if STORES_AT_END:
+        for h in range(2):
+            q.issue(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", f"w{h}")
     lines.append("s_mov_b32 m0, %[ms]")
     lines.append("s_waitcnt lgkmcnt(0)")
     # No padding: nothing reads the accumulators until after the sweep (the
