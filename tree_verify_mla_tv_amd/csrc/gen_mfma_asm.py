@@ -216,6 +216,12 @@ def softmax_valu():
 
     for k in range(8):
         op(f"v_cvt_pk_bf16_f32 {pk(k)}, {S(2 * k)}, {S(2 * k + 1)}")
+        if k % 4 == 3 and not STORES_AT_END:
+            # Store each half as soon as it is packed (listed early, so the
+            # scheduler issues it early and its latency hides behind the
+            # remaining value ops).
+            h = k // 4
+            op(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", lds=f"w{h}")
     # The row sum takes the rounded weights the value product uses: a bf16
     # value is its bits in the top half of an fp32 word, so each packed pair
     # unpacks with one shift and one mask, then plain fp32 adds in two chains
@@ -230,9 +236,6 @@ def softmax_valu():
         op(f"v_add_f32 {acc}, {acc}, {lo}")
         op(f"v_add_f32 {acc}, {acc}, {hi}")
     op(f"v_add_f32 %[l], %[l], {t[4]}")
-    if not STORES_AT_END:
-        for h in range(2):
-            op(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", lds=f"w{h}")
     return ops
 
 
