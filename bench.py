@@ -36,16 +36,21 @@ PEAKS_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32_mfma": 157.3, "f32_valu": 15
 # Which kernel the library runs for each cache dtype, the arithmetic it does,
 # and the roofline that bounds it.
 KERNELS = {
-    "bf16": dict(name="attn_mfma_bf16_kernel", source="tree_verify_mla_tv_amd/csrc/attn_mfma.hip", bound="mfma",
-                 peak="bf16", dtype="bf16"),
-    "f32": dict(name="attn_valu_kernel", source="tree_verify_mla_tv_amd/csrc/attn_valu.hip", bound="alu",
+    "bf16": dict(name="attn_mfma_bf16_kernel",
+                 source=["tree_verify_mla_tv_amd/csrc/attn_mfma.hip", "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h"],
+                 bound="mfma", peak="bf16", dtype="bf16"),
+    "f32": dict(name="attn_valu_kernel", source=["tree_verify_mla_tv_amd/csrc/attn_valu.hip"], bound="alu",
                 peak="f32_valu", dtype="f32"),
 }
 
 
-def source_hash(rel: str) -> str:
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(rels) -> str:
+    """First 16 hex digits of sha256 over the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_counts(w, parent) -> dict:
