@@ -65,3 +65,49 @@ def verify_attn_scalar(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, sm_scale
                     out[b][i][h][d] = math.fsum([e[t] * float(c_kv[b][j][d]) for t, j in enumerate(keys)]) / l
                 lse[b][i][h] = m + math.log(l)
     return out, lse
+
+
+# ----------------------------------------------------------------------------
+# Greedy accept, argmax and compaction (independent of oracle/accept_oracle.py)
+# ----------------------------------------------------------------------------
+def argmax_scalar(row):
+    """First index of the largest value; a NaN beats everything (first NaN wins);
+    -0.0 and +0.0 are equal.  A plain Python scan."""
+    best_i, best = 0, None
+    for i, v in enumerate(row):
+        v = float(v)
+        if best is None:
+            best_i, best = i, v
+            continue
+        if math.isnan(best):
+            continue
+        if math.isnan(v) or v > best:
+            best_i, best = i, v
+    return best_i
+
+
+def accept_scalar(parent_row, draft_row, target_row):
+    """Deepest node whose root path follows the target's greedy tokens, found by
+    checking every node's whole path (for trees without two siblings carrying
+    the same draft token, where that node is unique).
+
+    Returns (path as a list of node indices from the root, bonus token)."""
+    q = len(parent_row)
+    best = [0]
+    for v in range(q):
+        chain = [v]
+        while chain[-1] != 0:
+            chain.append(parent_row[chain[-1]])
+        chain.reverse()                      # root ... v
+        ok = all(draft_row[chain[k]] == target_row[chain[k - 1]] for k in range(1, len(chain)))
+        if ok and len(chain) > len(best):
+            best = chain
+    return best, target_row[best[-1]]
+
+
+def compact_scalar(rows, path, accept_len, prefix_len):
+    """rows: list of per-row values of one cache entry; returns the compacted list."""
+    out = list(rows)
+    for k in range(1, accept_len + 1):
+        out[prefix_len + k] = rows[prefix_len + path[k]]
+    return out
