@@ -154,6 +154,64 @@ tv_status_t tv_verify_step(const float* q_lat, float* q_rope, const void* c_kv, 
                            float* out, float* lse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * tv_argmax_rows — the target's greedy token per tree node: for each of n_rows
+ *   rows of logits [n_rows][vocab] (dtype TV_F32 or TV_BF16, row-major, dense),
+ *   out[r] = the index of the row's largest value, the lowest index on ties; a
+ *   NaN counts as larger than every number (the first NaN wins) and -0.0 equals
+ *   +0.0.  [RoPE page, "The Broader Context: A Full Native Engine from Scratch"
+ *   (greedy tree accept; the loop's greedy output must match autoregressive
+ *   greedy output)]
+ *   logits must be aligned to its element size; 16-byte aligned rows whose byte
+ *   length is a multiple of 16 take a vectorised path.  out: int32 [n_rows],
+ *   4-byte aligned.  n_rows = 0 is a no-op; n_rows > INT32_MAX returns
+ *   TV_ERR_UNSUPPORTED.
+ */
+tv_status_t tv_argmax_rows(const void* logits, tv_dtype_t dtype, int64_t n_rows, int32_t vocab, int32_t* out,
+                           hipStream_t stream);
+
+/*
+ * tv_tree_accept — greedy acceptance of each batch entry's draft tree.
+ *   [RoPE page, "The Broader Context: A Full Native Engine from Scratch";
+ *   Golden page, "Context: The Quest for a Hyper-Optimized Inference Stack"
+ *   (greedy tree-accept kernel) and "Recursive Refinement of the Decode Loop
+ *   Design" (root, draft and bonus tokens)]
+ *   Node 0 (the root) is already committed.  From the current node cur the
+ *   target's next token is target_tok[b][cur]; the walk moves to the child of
+ *   cur (parent[b][c] == cur) whose draft_tok[b][c] equals it -- the lowest
+ *   index c if several do -- and stops when none does.
+ *   Inputs (int32, [B][q_len], 4-byte aligned): parent (as for tv_verify_attn;
+ *   a node whose parent is outside [0, i) is never accepted), draft_tok (entry
+ *   0 is the root's token and is not compared), target_tok (the target's
+ *   greedy token after each node, e.g. from tv_argmax_rows).
+ *   Outputs: path [B][q_len] int32: path[b][0] = 0, then the accepted nodes in
+ *   order, then -1; accept_len [B] int32: accepted draft nodes; bonus_tok [B]
+ *   int32: target_tok at the last accepted node.  The step commits the draft
+ *   tokens of path[b][1..accept_len] and then bonus_tok.
+ *   1 <= q_len <= TV_MAX_Q_LEN.
+ */
+tv_status_t tv_tree_accept(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok, int32_t B,
+                           int32_t q_len, int32_t* path, int32_t* accept_len, int32_t* bonus_tok, hipStream_t stream);
+
+/*
+ * tv_kv_compact — post-verify compaction of the latent cache, in place.
+ *   [RoPE page, "The Broader Context: A Full Native Engine from Scratch" (KV
+ *   cache with post-verify compaction)]
+ *   For each b and k = 1 .. accept_len[b]: row prefix_len + k of c_kv[b] and of
+ *   k_rope[b] takes row prefix_len + path[b][k] (the tv_tree_accept outputs);
+ *   every other row is unchanged.  The accepted path's node k has depth k, so
+ *   its rope row (rotated at prefix_len + depth) is already right for its new
+ *   row.  The next step's prefix is prefix_len + accept_len + 1 rows.
+ *   c_kv [B][kv_len][d_c], k_rope [B][kv_len][d_r] (kv_dtype), 16-byte aligned,
+ *   with d_c and d_r rows a multiple of 16 bytes (else TV_ERR_UNSUPPORTED);
+ *   prefix_len + q_len <= kv_len.  path [B][q_len] and accept_len [B] int32 are
+ *   device data: accept_len is clamped to [0, q_len - 1] and path entries to
+ *   [0, q_len - 1], so malformed values move rows of the tree only.
+ */
+tv_status_t tv_kv_compact(void* c_kv, void* k_rope, tv_dtype_t kv_dtype, const int32_t* path,
+                          const int32_t* accept_len, int32_t prefix_len, int32_t B, int32_t kv_len, int32_t q_len,
+                          int32_t d_c, int32_t d_r, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("tv_rope_neox", "tv_verify_attn", "tv_verify_attn_workspace_size", "tv_status_str",
-              "tv_tree_positions", "tv_verify_step", "tv_tree_rope"):
+              "tv_tree_positions", "tv_verify_step", "tv_tree_rope", "tv_argmax_rows", "tv_tree_accept",
+              "tv_kv_compact"):
         assert s in syms
 
 
@@ -127,3 +128,37 @@ def test_tree_rope_rejects_before_launch():
     assert r(None, A, 0, A, 4, 1, 2, 3, 64, 1e4, None) == INV
     assert r(A, A + 4, 0, A, 4, 1, 2, 3, 64, 1e4, None) == INV  # misaligned
     assert r(A, A, 0, A, -1, 1, 2, 3, 64, 1e4, None) == INV
+
+
+def test_argmax_rows_rejects_before_launch():
+    f = tv.load().tv_argmax_rows
+    assert f(A, 0, 0, 10, A, None) == OK                   # no rows: nothing to do
+    assert f(None, 0, 3, 10, A, None) == INV
+    assert f(A, 0, 3, 10, None, None) == INV
+    assert f(A, 0, 3, 0, A, None) == INV                   # empty vocabulary
+    assert f(A, 0, -1, 10, A, None) == INV
+    assert f(A, 5, 3, 10, A, None) == INV                  # dtype
+    assert f(A + 2, 0, 3, 10, A, None) == INV              # f32 logits not 4-byte aligned
+    assert f(A + 1, 1, 3, 10, A, None) == INV              # bf16 logits not 2-byte aligned
+    assert f(A, 0, 3, 10, A + 2, None) == INV
+    assert f(A, 0, 2**31, 10, A, None) == UNS
+
+
+def test_tree_accept_rejects_before_launch():
+    f = tv.load().tv_tree_accept
+    assert f(None, A, A, 1, 3, A, A, A, None) == INV
+    assert f(A, A, A, 0, 3, A, A, A, None) == INV
+    assert f(A, A, A, 1, 0, A, A, A, None) == INV
+    assert f(A, A, A, 1, 65, A, A, A, None) == UNS
+    assert f(A, A, A + 2, 1, 3, A, A, A, None) == INV
+    assert f(A, A, A, 1, 3, A, None, A, None) == INV
+
+
+def test_kv_compact_rejects_before_launch():
+    f = tv.load().tv_kv_compact
+    assert f(None, A, 1, A, A, 4, 1, 7, 3, 512, 64, None) == INV
+    assert f(A, A, 1, A, A, 5, 1, 7, 3, 512, 64, None) == INV          # prefix + q_len > kv_len
+    assert f(A, A, 1, A, A, 4, 1, 7, 65, 512, 64, None) == UNS
+    assert f(A, A, 1, A, A, 4, 1, 7, 3, 12, 64, None) == UNS           # 24-byte rows
+    assert f(A + 8, A, 1, A, A, 4, 1, 7, 3, 512, 64, None) == INV      # c_kv not 16-byte aligned
+    assert f(A, A, 9, A, A, 4, 1, 7, 3, 512, 64, None) == INV          # dtype

@@ -182,4 +182,52 @@ tv_status_t tv_verify_step(const float* q_lat, float* q_rope, const void* c_kv, 
                        out, lse, workspace, workspace_bytes, stream);
 }
 
+tv_status_t tv_argmax_rows(const void* logits, tv_dtype_t dtype, int64_t n_rows, int32_t vocab, int32_t* out,
+                           hipStream_t stream) {
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID;
+  if (n_rows < 0 || vocab < 1) return TV_ERR_INVALID;
+  if (n_rows > INT32_MAX) return TV_ERR_UNSUPPORTED;
+  if (n_rows == 0) return TV_OK;
+  if (!logits || !out || (reinterpret_cast<uintptr_t>(out) & 3u)) return TV_ERR_INVALID;
+  const int elem = dtype == TV_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(logits) & static_cast<uintptr_t>(elem - 1)) return TV_ERR_INVALID;
+  // 16-byte loads when every row starts 16-byte aligned and is whole 16-byte chunks.
+  const bool vec = aligned16(logits) && (static_cast<int64_t>(vocab) * elem) % 16 == 0;
+  return tv::launch_argmax_rows(logits, dtype == TV_BF16, vec, n_rows, vocab, out, stream) == hipSuccess
+             ? TV_OK
+             : TV_ERR_LAUNCH;
+}
+
+tv_status_t tv_tree_accept(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok, int32_t B,
+                           int32_t q_len, int32_t* path, int32_t* accept_len, int32_t* bonus_tok, hipStream_t stream) {
+  if (B < 1 || q_len < 1) return TV_ERR_INVALID;
+  if (q_len > TV_MAX_Q_LEN) return TV_ERR_UNSUPPORTED;
+  const void* ptrs[] = {parent, draft_tok, target_tok, path, accept_len, bonus_tok};
+  for (const void* p : ptrs)
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 3u)) return TV_ERR_INVALID;
+  return tv::launch_tree_accept(parent, draft_tok, target_tok, B, q_len, path, accept_len, bonus_tok, stream) ==
+                 hipSuccess
+             ? TV_OK
+             : TV_ERR_LAUNCH;
+}
+
+tv_status_t tv_kv_compact(void* c_kv, void* k_rope, tv_dtype_t kv_dtype, const int32_t* path,
+                          const int32_t* accept_len, int32_t prefix_len, int32_t B, int32_t kv_len, int32_t q_len,
+                          int32_t d_c, int32_t d_r, hipStream_t stream) {
+  if (kv_dtype != TV_F32 && kv_dtype != TV_BF16) return TV_ERR_INVALID;
+  if (B < 1 || q_len < 1 || prefix_len < 0 || d_c < 1 || d_r < 1) return TV_ERR_INVALID;
+  if (q_len > TV_MAX_Q_LEN) return TV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(prefix_len) + q_len > kv_len) return TV_ERR_INVALID;
+  const int elem = kv_dtype == TV_BF16 ? 2 : 4;
+  if ((d_c * elem) % 16 != 0 || (d_r * elem) % 16 != 0) return TV_ERR_UNSUPPORTED;
+  if (!c_kv || !k_rope || !path || !accept_len) return TV_ERR_INVALID;
+  if (!aligned16(c_kv) || !aligned16(k_rope) || (reinterpret_cast<uintptr_t>(path) & 3u) ||
+      (reinterpret_cast<uintptr_t>(accept_len) & 3u))
+    return TV_ERR_INVALID;
+  return tv::launch_kv_compact(c_kv, k_rope, elem, path, accept_len, prefix_len, B, kv_len, q_len, d_c, d_r,
+                               stream) == hipSuccess
+             ? TV_OK
+             : TV_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -141,6 +141,14 @@ __device__ __forceinline__ long long unit_of_block(const AttnArgs& a, long long 
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 
+// The steps after verify (accept.hip).
+hipError_t launch_argmax_rows(const void* logits, bool bf16, bool vec, int64_t n_rows, int vocab, int32_t* out,
+                              hipStream_t stream);
+hipError_t launch_tree_accept(const int32_t* parent, const int32_t* draft, const int32_t* target, int B, int q_len,
+                              int32_t* path, int32_t* accept_len, int32_t* bonus, hipStream_t stream);
+hipError_t launch_kv_compact(void* c_kv, void* k_rope, int elem_bytes, const int32_t* path, const int32_t* accept_len,
+                             int prefix_len, int B, int kv_len, int q_len, int d_c, int d_r, hipStream_t stream);
+
 // Kernel launchers (one per kernel family).
 hipError_t launch_attn_valu(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_mfma_bf16(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);

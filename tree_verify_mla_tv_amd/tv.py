@@ -38,6 +38,9 @@ SIGNATURES = {
     "tv_tree_rope": (_i32, [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f64, _p]),
     "tv_verify_step": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f64, _f32, _p, _p,
                               _p, _sz, _p]),
+    "tv_argmax_rows": (_i32, [_p, _i32, _i64, _i32, _p, _p]),
+    "tv_tree_accept": (_i32, [_p, _p, _p, _i32, _i32, _p, _p, _p, _p]),
+    "tv_kv_compact": (_i32, [_p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
 }
 
 
@@ -226,3 +229,52 @@ def verify_step(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, theta: flo
         _ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
         float(theta), float(sm_scale), _ptr(out), _ptr(lse_t), _ptr(workspace), ws_n, _stream()))
     return (out, lse_t) if (return_lse or lse is not None) else out
+
+
+def argmax_rows(logits: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The target's greedy token per row of logits [..., vocab] (float32 or
+    bfloat16): int32 [...], lowest index on ties, a NaN beats every number."""
+    _cuda_contig("logits", logits)
+    dt = _kv_dtype(logits)
+    vocab = logits.shape[-1]
+    n_rows = logits.numel() // vocab
+    if out is None:
+        out = torch.empty(logits.shape[:-1], dtype=torch.int32, device=logits.device)
+    _cuda_contig("out", out)
+    _need(out.dtype == torch.int32 and out.numel() == n_rows, "out must be int32 with one entry per row")
+    _check("tv_argmax_rows", load().tv_argmax_rows(_ptr(logits), dt, n_rows, vocab, _ptr(out), _stream()))
+    return out
+
+
+def tree_accept(parent: torch.Tensor, draft_tok: torch.Tensor, target_tok: torch.Tensor):
+    """Greedy acceptance per tree: returns (path [B, q] int32, accept_len [B]
+    int32, bonus [B] int32).  All inputs int32 [B, q_len]."""
+    for n, t in (("parent", parent), ("draft_tok", draft_tok), ("target_tok", target_tok)):
+        _cuda_contig(n, t)
+        _need(t.dtype == torch.int32 and t.dim() == 2, f"{n} must be int32 [B, q_len]")
+    B, q = parent.shape
+    _need(draft_tok.shape == (B, q) and target_tok.shape == (B, q), "inputs must share the shape [B, q_len]")
+    path = torch.empty_like(parent)
+    accept_len = torch.empty(B, dtype=torch.int32, device=parent.device)
+    bonus = torch.empty(B, dtype=torch.int32, device=parent.device)
+    _check("tv_tree_accept", load().tv_tree_accept(_ptr(parent), _ptr(draft_tok), _ptr(target_tok), B, q, _ptr(path),
+                                                   _ptr(accept_len), _ptr(bonus), _stream()))
+    return path, accept_len, bonus
+
+
+def kv_compact(c_kv: torch.Tensor, k_rope: torch.Tensor, path: torch.Tensor, accept_len: torch.Tensor,
+               prefix_len: int):
+    """Move the accepted nodes' rows of c_kv [B, kv, d_c] and k_rope [B, kv, d_r]
+    to rows prefix_len + 1 .. prefix_len + accept_len, in place."""
+    for n, t in (("c_kv", c_kv), ("k_rope", k_rope), ("path", path), ("accept_len", accept_len)):
+        _cuda_contig(n, t)
+    _need(c_kv.dtype == k_rope.dtype, "c_kv and k_rope must share a dtype")
+    _need(path.dtype == torch.int32 and accept_len.dtype == torch.int32, "path and accept_len must be int32")
+    B, kv, d_c = c_kv.shape
+    _need(k_rope.dim() == 3 and k_rope.shape[:2] == (B, kv), "k_rope must be [B, kv, d_r]")
+    _need(path.dim() == 2 and path.shape[0] == B and accept_len.shape == (B,), "path [B, q_len], accept_len [B]")
+    q = path.shape[1]
+    _check("tv_kv_compact", load().tv_kv_compact(_ptr(c_kv), _ptr(k_rope), _kv_dtype(c_kv), _ptr(path),
+                                                 _ptr(accept_len), prefix_len, B, kv, q, d_c, k_rope.shape[2],
+                                                 _stream()))
+    return c_kv, k_rope

@@ -159,3 +159,66 @@ def make_inputs(w: Workload | str, seed: int | None = None, batch: int | None = 
     return dict(q_lat=q_lat, q_rope=q_rope, c_kv=c_kv, k_rope=k_rope, parent=parent,
                 prefix_len=w.prefix_len, theta=w.theta, sm_scale=w.sm_scale,
                 kv_dtype=w.kv_dtype, workload=w)
+
+
+# ----------------------------------------------------------------------------
+# Inputs of the steps after verify (greedy tokens, tree accept, compaction)
+# ----------------------------------------------------------------------------
+SERVE_VOCAB = 163840  # a K2-class vocabulary; the pages print only the tiny model's (512)
+
+
+def make_accept_inputs(parent: np.ndarray, vocab: int, seed: int, logits_dtype: str = "f32",
+                       max_accept: int | None = None) -> dict:
+    """Synthetic draft tokens and target logits for trees ``parent`` [B, q].
+
+    Recipe: ``numpy.random.default_rng(seed)``.  Each node's draft token is drawn
+    uniformly, redrawn until it differs from its earlier siblings' (as a
+    best-first drafter's top-k children do).  Logits are N(0,1) fp32 per node
+    over the vocabulary.  For each tree a target path is planted: from the root,
+    a uniformly chosen child is followed for a depth drawn uniformly from
+    [0, min(max depth, max_accept)]; along it, each node's logits get +8 at the
+    next path node's draft token (so the target's greedy token there is that
+    draft token), and the last path node gets +8 at a token no child of it
+    carries.  bf16 logits are the fp32 draw rounded to nearest-even bf16 (uint16
+    bit patterns).  Returns draft [B, q] int32, logits [B, q, vocab] (float32 or
+    uint16) and the planted depth [B].
+    """
+    rng = np.random.default_rng(seed)
+    p = np.asarray(parent)
+    B, q = p.shape
+    draft = np.zeros((B, q), dtype=np.int32)
+    for b in range(B):
+        kids = {}
+        for i in range(q):
+            taken = kids.setdefault(int(p[b, i]), set())
+            while True:
+                t = int(rng.integers(0, vocab))
+                if t not in taken or i == 0:
+                    break
+            taken.add(t)
+            draft[b, i] = t
+    logits = rng.standard_normal((B, q, vocab), dtype=np.float32)
+    depth = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        children = [[c for c in range(1, q) if p[b, c] == v] for v in range(q)]
+        longest = [0] * q
+        for v in range(q - 1, -1, -1):
+            longest[v] = 1 + max((longest[c] for c in children[v]), default=-1) if children[v] else 0
+        cap = longest[0] if max_accept is None else min(longest[0], max_accept)
+        want = int(rng.integers(0, cap + 1))
+        cur = 0
+        for _ in range(want):
+            opts = [c for c in children[cur] if longest[c] >= want - depth[b] - 1]
+            nxt = opts[int(rng.integers(0, len(opts)))]
+            logits[b, cur, draft[b, nxt]] += 8.0
+            cur = nxt
+            depth[b] += 1
+        kid_toks = {int(draft[b, c]) for c in children[cur]}
+        while True:
+            t = int(rng.integers(0, vocab))
+            if t not in kid_toks:
+                break
+        logits[b, cur, t] += 8.0
+    if logits_dtype == "bf16":
+        logits = f32_to_bf16_bits(logits)
+    return {"draft": draft, "logits": logits, "depth": depth}
