@@ -117,6 +117,58 @@ def copy_calibration(torch) -> int:
     return 0
 
 
+def _time_ms(torch, fn, reps: int) -> float:
+    """Mean ms per call over reps calls, HIP events on the current stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, with_oracle: bool) -> dict:
+    """The steps after verify on the same batch: the target's greedy token per
+    node over a K2-class vocabulary (fp32 logits), greedy tree accept, and
+    compaction of the accepted rows of the bf16 cache."""
+    import numpy as np
+    dev = c_kv.device
+    x = W.make_accept_inputs(inp["parent"], W.SERVE_VOCAB, seed=1234)
+    logits = torch.from_numpy(x["logits"]).to(dev)
+    draft = torch.from_numpy(x["draft"]).to(dev)
+    target = torch.empty(w.B, w.q_len, dtype=torch.int32, device=dev)
+    ms_argmax = _time_ms(torch, lambda: tv.argmax_rows(logits, out=target), 20)
+    path, n, bonus = tv.tree_accept(parent, draft, target)
+    ms_accept = _time_ms(torch, lambda: tv.tree_accept(parent, draft, target), 50)
+    c2, r2 = c_kv.clone(), k_rope.clone()
+    ms_compact = _time_ms(torch, lambda: tv.kv_compact(c2, r2, path, n, w.prefix_len), 50)
+    n_host = n.cpu().numpy()
+    logit_bytes = logits.numel() * 4
+    moved_bytes = int(n_host.sum()) * 2 * (w.d_c + w.d_r) * 2
+    out = {
+        "workload": f"B={w.B} q_len={w.q_len} vocab={W.SERVE_VOCAB} fp32 logits; bf16 cache d_c={w.d_c} d_r={w.d_r}",
+        "argmax_rows": {"ms": round(ms_argmax, 4), "bytes": logit_bytes,
+                        "achieved_gbs": round(logit_bytes / (ms_argmax * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(logit_bytes / (ms_argmax * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "tree_accept": {"ms": round(ms_accept, 4), "accepted_mean": round(float(n_host.mean()), 3),
+                        "bound": "launch latency (integer walk, one wave per tree)"},
+        "kv_compact": {"ms": round(ms_compact, 4), "bytes_moved": moved_bytes,
+                       "bound": "launch latency (a few hundred KB)"},
+    }
+    if with_oracle:
+        from oracle import accept_oracle as A
+        t0 = time.perf_counter()
+        tg = A.greedy_tokens(x["logits"][:4])
+        A.tree_accept(inp["parent"][:4], x["draft"][:4], tg)
+        dt = (time.perf_counter() - t0) * w.B / 4
+        out["cpu_oracle_ms"] = {"value": round(dt * 1e3, 1), "sample": "greedy tokens + accept on 4 of 32 trees, "
+                                                                       "scaled x8"}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +176,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-sample", type=int, default=6, help="trees the CPU oracle times (0 = skip)")
+    ap.add_argument("--no-next-rows", dest="next_rows", action="store_false",
+                    help="skip timing the steps after verify (greedy tokens, tree accept, KV compaction)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the reference launch that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -232,6 +286,8 @@ def main() -> int:
     }
     if args.cpu_sample > 0:
         rec["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_sample, w.B))
+    if args.next_rows and w.kv_dtype == "bf16":
+        rec["next_rows"] = next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, args.cpu_sample > 0)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -38,6 +38,22 @@ __device__ __forceinline__ float load_logit(const void* row, int64_t i) {
   return static_cast<const float*>(row)[i];
 }
 
+// Running maximum of one thread, which sees its indices in increasing order:
+// a value replaces the best if it is larger, or if it is the first NaN, so the
+// first index wins ties (-0.0 == +0.0 under '>') and the first NaN wins.
+struct Best {
+  float v = -INFINITY;
+  int i = -1;  // -1: nothing seen yet
+  __device__ __forceinline__ void see(float x, int idx) {
+    const bool take = (i < 0) | (x > v) | ((x != x) & (v == v));
+    v = take ? x : v;
+    i = take ? idx : i;
+  }
+  __device__ __forceinline__ unsigned long long packed() const {
+    return i < 0 ? 0ull : pack(float_key(v), static_cast<uint32_t>(i));
+  }
+};
+
 // One workgroup (256 threads) per row.  VEC: the row is 16-byte aligned and a
 // whole number of 16-byte chunks (4 floats or 8 bf16), read with 16-byte loads.
 template <bool BF16, bool VEC>
@@ -48,25 +64,23 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const void* __restrict
   const int64_t row = blockIdx.x;
   if (row >= n_rows) return;
   const unsigned char* base = static_cast<const unsigned char*>(logits) + row * static_cast<int64_t>(vocab) * kElem;
-  unsigned long long best = 0;
+  Best best;
   if (VEC) {
     const int chunks = vocab / kPerChunk;
     const uint4* p = reinterpret_cast<const uint4*>(base);
     int c = threadIdx.x;
-    // Four chunks in flight per thread.
-    for (; c + 3 * 256 < chunks; c += 4 * 256) {
-      uint4 v[4];
+    // Eight 16-byte chunks in flight per thread.
+    for (; c + 7 * 256 < chunks; c += 8 * 256) {
+      uint4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = p[c + u * 256];
+      for (int u = 0; u < 8; ++u) v[u] = p[c + u * 256];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
         const int i0 = (c + u * 256) * kPerChunk;
 #pragma unroll
-        for (int e = 0; e < kPerChunk; ++e) {
-          const float x = BF16 ? __uint_as_float((w[e / 2] >> (16 * (e & 1))) << 16) : __uint_as_float(w[e]);
-          best = umax64(best, pack(float_key(x), static_cast<uint32_t>(i0 + e)));
-        }
+        for (int e = 0; e < kPerChunk; ++e)
+          best.see(BF16 ? __uint_as_float((w[e / 2] >> (16 * (e & 1))) << 16) : __uint_as_float(w[e]), i0 + e);
       }
     }
     for (; c < chunks; c += 256) {
@@ -74,24 +88,22 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const void* __restrict
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       const int i0 = c * kPerChunk;
 #pragma unroll
-      for (int e = 0; e < kPerChunk; ++e) {
-        const float x = BF16 ? __uint_as_float((w[e / 2] >> (16 * (e & 1))) << 16) : __uint_as_float(w[e]);
-        best = umax64(best, pack(float_key(x), static_cast<uint32_t>(i0 + e)));
-      }
+      for (int e = 0; e < kPerChunk; ++e)
+        best.see(BF16 ? __uint_as_float((w[e / 2] >> (16 * (e & 1))) << 16) : __uint_as_float(w[e]), i0 + e);
     }
   } else {
-    for (int i = threadIdx.x; i < vocab; i += 256)
-      best = umax64(best, pack(float_key(load_logit<BF16>(base, i)), static_cast<uint32_t>(i)));
+    for (int i = threadIdx.x; i < vocab; i += 256) best.see(load_logit<BF16>(base, i), i);
   }
-  // Wave, then workgroup maximum.
+  // Across threads: (key, inverted index) maximum, wave then workgroup.
+  unsigned long long m = best.packed();
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) best = umax64(best, __shfl_xor(best, off));
+  for (int off = 32; off > 0; off >>= 1) m = umax64(m, __shfl_xor(m, off));
   __shared__ unsigned long long s_best[4];
-  if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = best;
+  if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned long long m = umax64(umax64(s_best[0], s_best[1]), umax64(s_best[2], s_best[3]));
-    out[row] = static_cast<int32_t>(~static_cast<uint32_t>(m & 0xffffffffu));
+    const unsigned long long r = umax64(umax64(s_best[0], s_best[1]), umax64(s_best[2], s_best[3]));
+    out[row] = static_cast<int32_t>(~static_cast<uint32_t>(r & 0xffffffffu));
   }
 }
 
