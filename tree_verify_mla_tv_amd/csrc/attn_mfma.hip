@@ -372,25 +372,43 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   }
   __syncthreads();
 
+  // Output, one row block (32 rows x 512 columns, fp32) at a time, through LDS
+  // so that every store instruction writes whole rows: each wave drops its 128
+  // columns of the 32 rows (normalised by the row sum) into the idle tile
+  // buffers, rows 0-15 in g_k0 and 16-31 in g_k1 at a 2064-byte pitch (16 rows
+  // of 128-bit writes hit 16 different bank groups); then all 256 threads copy
+  // two 2 KB rows per pass, 16 bytes each, to HBM.
+  constexpr int kOutPitch = mf::DC * 4 + 16;
+  const int rl = lane & 31;
+  unsigned char* const stage_row = (rl < 16 ? g_k0 : g_k1) + (rl & 15) * kOutPitch;
+  const int c16 = threadIdx.x & 127;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    const int r = w.rb * kMfmaRows + rb * 32 + (lane & 31);
-    if (r < a.R) {
-      const float lr = s_row_l[rb * 32 + (lane & 31)];
-      const float inv = lr > 0.f ? 1.f / lr : 0.f;
-      float* dst = w.slot < 0 ? a.out + (tree_row0 + r) * mf::DC
-                              : a.ws_o + (w.slot * kMfmaRows + rb * 32 + (lane & 31)) * mf::DC;
-      dst += 128 * wave + 32 * g2;
+    const float lr = s_row_l[rb * 32 + rl];
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const f32x16_t& v = o[4 * rb + db];
+    for (int db = 0; db < 4; ++db) {
+      const f32x16_t& v = o[4 * rb + db];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          *reinterpret_cast<float4*>(dst + 64 * (q4 & 1) + 8 * db + 4 * (q4 >> 1)) =
-              make_float4(v[4 * q4] * inv, v[4 * q4 + 1] * inv, v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv);
-        }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = 128 * wave + 32 * g2 + 64 * (q4 & 1) + 8 * db + 4 * (q4 >> 1);
+        *reinterpret_cast<float4*>(stage_row + col * 4) =
+            make_float4(v[4 * q4] * inv, v[4 * q4 + 1] * inv, v[4 * q4 + 2] * inv, v[4 * q4 + 3] * inv);
       }
     }
+    __syncthreads();
+#pragma unroll 4
+    for (int pass = 0; pass < 16; ++pass) {
+      const int rr = 2 * pass + (threadIdx.x >> 7);  // row within the block
+      const int r = w.rb * kMfmaRows + rb * 32 + rr;
+      if (r < a.R) {
+        const float4 v = *reinterpret_cast<const float4*>((rr < 16 ? g_k0 : g_k1) + (rr & 15) * kOutPitch + c16 * 16);
+        float* dst = w.slot < 0 ? a.out + (tree_row0 + r) * mf::DC
+                                : a.ws_o + (w.slot * kMfmaRows + rb * 32 + rr) * mf::DC;
+        reinterpret_cast<float4*>(dst)[c16] = v;
+      }
+    }
+    __syncthreads();
   }
 }
 

@@ -72,6 +72,7 @@ CLOBBERED = list(range(S_BASE, 256))
 AHEAD = 6        # a fragment is read at most this many matrix ops before its first use
 QK_COPY_GROUPS = 18   # copy groups issued among the score ops; the rest go among the value ops
 VALU_PER_GAP = 4      # softmax ops between two value ops
+TRANS_PER_GAP = 3     # of which v_exp_f32
 STORES_AT_END = False # weights stored after the last value op instead of between them
 NOP_AFTER = "s_nop 7\\n s_nop 7\\n s_nop 7\\n"   # >= 19 wait states after the last MFMA
 NEG_INF = "0xff800000"
@@ -239,38 +240,54 @@ def softmax_valu():
     return ops
 
 
-def schedule_valu(ops, n_slots, first_slot, per_slot):
+def schedule_valu(ops, n_slots, first_slot, per_slot, trans_per_slot=3):
     """Greedy list schedule of the VALU graph into the gaps after matrix ops:
-    at most per_slot ops per gap, and an op never shares a gap with an op it
-    reads (a matrix op, >= 32 cycles, sits between producer and consumer)."""
+    at most per_slot ops (and trans_per_slot transcendentals) per gap, and an
+    op never shares a gap with an op it reads (a matrix op, >= 32 cycles, sits
+    between producer and consumer)."""
     slot_of = {}
     out = [[] for _ in range(n_slots)]
     pending = list(range(len(ops)))
     for sl in range(first_slot, n_slots):
-        placed = 0
+        placed = trans = 0
         for i in list(pending):
             if placed == per_slot:
                 break
+            is_trans = ops[i][0].startswith("v_exp")
+            if is_trans and trans == trans_per_slot:
+                continue
             if all(d in slot_of and slot_of[d] < sl for d in ops[i][2]):
                 slot_of[i] = sl
                 out[sl].append(ops[i])
                 pending.remove(i)
                 placed += 1
+                trans += is_trans
         if not pending:
             break
     assert not pending, "softmax does not fit between the value ops"
     return out
 
 
+def mask_branch():
+    """Entry to the mask: a branch taken only when %[nm] != 0 (tiles holding
+    tree keys or the unit's range end).  The mask code itself sits out of line
+    after the block's last instruction (mask_block), so the common path runs
+    straight through: a taken branch here would stall instruction fetch right
+    behind the first value MFMA on every step."""
+    return ["s_cmp_lg_u32 %[nm], 0", "s_cbranch_scc1 .Ltv_mask_%=", ".Ltv_masked_%=:"]
+
+
 def mask_block():
+    """Out-of-line mask code: score i becomes -inf unless bit i of %[mask] is
+    set; then back into the block."""
     # -inf in a register: v_cndmask with VCC has no constant-bus slot left
     # for a literal.
     t0, t1 = f"v{TMP[0]}", f"v{TMP[1]}"
-    lines = ["s_cmp_eq_u32 %[nm], 0", "s_cbranch_scc1 .Ltv_nomask_%=", f"v_mov_b32 {t0}, {NEG_INF}"]
+    lines = [".Ltv_mask_%=:", f"v_mov_b32 {t0}, {NEG_INF}"]
     for i in range(16):
         lines += [f"v_bfe_u32 {t1}, %[mask], {i}, 1", f"v_cmp_ne_u32 vcc, 0, {t1}",
                   f"v_cndmask_b32 {S(i)}, {t0}, {S(i)}, vcc"]
-    lines.append(".Ltv_nomask_%=:")
+    lines.append("s_branch .Ltv_masked_%=")
     return lines
 
 
@@ -327,7 +344,7 @@ def step_asm() -> str:
     # VALU work between value ops: the S hazard padding and the (optional)
     # mask after the first one, then the dependency graph, list-scheduled.
     n_pv = 32
-    per_op = schedule_valu(valu, n_pv, 1, VALU_PER_GAP)
+    per_op = schedule_valu(valu, n_pv, 1, VALU_PER_GAP, TRANS_PER_GAP)
 
     nxt = 0
     for m, (kind, idx) in enumerate(mfma):
@@ -355,7 +372,7 @@ def step_asm() -> str:
                 # The last score op wrote S one value op ago: >= 19 wait
                 # states before the first VALU read of S.
                 lines.append("s_nop 7\\n s_nop 7\\n s_nop 4")
-                lines.extend(mask_block())
+                lines.extend(mask_branch())
             if n < len(stage_pv):
                 lines.extend(stage_pv[n])
             for text, lds_name, _ in per_op[n]:
@@ -369,8 +386,12 @@ def step_asm() -> str:
             q.issue(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", f"w{h}")
     lines.append("s_mov_b32 m0, %[ms]")
     lines.append("s_waitcnt lgkmcnt(0)")
-    # No padding: nothing reads the accumulators until after the sweep (the
-    # kernel pads once there, TV_MFMA_DRAIN_ASM).
+    # The out-of-line mask code, jumped over (the only taken branch on the
+    # common path, behind the last MFMA).  No padding: nothing reads the
+    # accumulators until after the sweep (TV_MFMA_DRAIN_ASM there).
+    lines.append("s_branch .Ltv_end_%=")
+    lines.extend(mask_block())
+    lines.append(".Ltv_end_%=:")
     return "\\n".join(lines) + "\\n"
 
 
