@@ -71,8 +71,9 @@ TMP = list(range(248, 256))                   # v[248:255]: VALU temporaries
 CLOBBERED = list(range(S_BASE, 256))
 AHEAD = 6        # a fragment is read at most this many matrix ops before its first use
 QK_COPY_GROUPS = 18   # copy groups issued among the score ops; the rest go among the value ops
-VALU_PER_GAP = 4      # softmax ops between two value ops
+GAP_BUDGET = 5        # instructions between two value MFMAs (one wave per SIMD issues ~1 per 4 cycles; an MFMA is 32)
 TRANS_PER_GAP = 3     # of which v_exp_f32
+S_HAZARD = 12         # wait states from the last score MFMA to the first VALU read of S
 STORES_AT_END = False # weights stored after the last value op instead of between them
 NOP_AFTER = "s_nop 7\\n s_nop 7\\n s_nop 7\\n"   # >= 19 wait states after the last MFMA
 NEG_INF = "0xff800000"
@@ -314,73 +315,139 @@ def step_asm() -> str:
     for fr, m in last_use.items():
         release.setdefault(m + 2, []).append(fr)
 
-    lines = ["s_mov_b32 %[ms], m0"]
-    q = LdsQueue(lines)
+    # Pass 1: the LDS fragment loads.  Before matrix op m, every fragment whose
+    # first use is at most AHEAD ops away is loaded, while the pool has quads.
     free = list(POOL)
     where = {}
+    loads_before = [[] for _ in mfma]
+    nxt = 0
+    for m in range(len(mfma)):
+        for fr in release.get(m, []):
+            free.append(where[fr])
+        while nxt < len(order) and first_use[order[nxt]] <= m + AHEAD and free:
+            where[order[nxt]] = free.pop(0)
+            loads_before[m].append(order[nxt])
+            nxt += 1
+    assert nxt == len(order)
+
+    lines = ["s_mov_b32 %[ms], m0"]
+    q = LdsQueue(lines)
+    ws = [None]   # wait states (instructions) since the last score MFMA
+
+    def emit(text, lds_name=None):
+        if lds_name:
+            q.issue(text, lds_name)
+        else:
+            lines.append(text)
+        if ws[0] is not None:
+            ws[0] += sum(int(t.split()[1]) + 1 if t.strip().startswith("s_nop") else 1
+                         for t in text.split("\\n") if t.strip() and not t.strip().endswith(":"))
 
     def load(fr):
-        r = free.pop(0)
-        where[fr] = r
+        r = where[fr]
         kind, idx = fr[0], fr[1:]
         if kind == "K":
             ks = int(idx)
             src = f"%[lat] offset:{32 * ks}" if ks < 32 else f"%[rope] offset:{256 * (ks - 32)}"
-            q.issue(f"ds_read_b128 {quad(r)}, {src}", fr)
+            emit(f"ds_read_b128 {quad(r)}, {src}", fr)
         elif kind == "R":
-            q.issue(f"ds_read_b128 {quad(r)}, %[qr] offset:{4096 * int(idx)}", fr)
+            emit(f"ds_read_b128 {quad(r)}, %[qr] offset:{4096 * int(idx)}", fr)
         elif kind == "V":
             f = int(idx)
             off = 16640 * (f >> 2) + 16 * (f & 3)
-            q.issue(f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[tb] offset:{off}", fr + "lo")
-            q.issue(f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[tb] offset:{off + 8320}", fr)
+            emit(f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[tb] offset:{off}", fr + "lo")
+            emit(f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[tb] offset:{off + 8320}", fr)
         else:  # P<rb><h>
             rb, h = int(idx[0]), int(idx[1])
-            q.issue(f"ds_read_b128 {quad(r)}, %[pb] offset:{1024 * (2 * rb + h)}", fr)
+            emit(f"ds_read_b128 {quad(r)}, %[pb] offset:{1024 * (2 * rb + h)}", fr)
+
+    def n_instr(fr):
+        return 2 if fr[0] == "V" else 1
 
     stage = stage_ops()
     stage_qk, stage_pv = stage[:QK_COPY_GROUPS], stage[QK_COPY_GROUPS:]
     valu = softmax_valu()
-    # VALU work between value ops: the S hazard padding and the (optional)
-    # mask after the first one, then the dependency graph, list-scheduled.
-    n_pv = 32
-    per_op = schedule_valu(valu, n_pv, 1, VALU_PER_GAP, TRANS_PER_GAP)
+    s_regs = {S(i) for i in range(16)}
+    reads_s = [any(r in s_regs for r in _reads_writes(t)[0]) for t, _, _ in valu]
+    # The mask code overwrites VCC and two temporaries: an op that touches
+    # them, like one that reads S, must come after the mask branch.
+    mask_regs = {"vcc", f"v{TMP[0]}", f"v{TMP[1]}"}
+    after_mask = [reads_s[i] or any(r in mask_regs for rw in _reads_writes(t) for r in rw)
+                  for i, (t, _, _) in enumerate(valu)]
+    pending = list(range(len(valu)))
+    gap_of = {}
+    masked = [False]
 
-    nxt = 0
+    def fill_gap(n, budget, last):
+        """List-schedule VALU ops into the gap after value op n: at most budget
+        instructions, TRANS_PER_GAP transcendentals, and no op in the same gap
+        as an op it depends on, so a matrix op (32 cycles) covers each
+        producer's latency and hazard.  The first read of S comes
+        >= S_HAZARD wait states after the last score MFMA, padded with s_nop
+        if nothing else fills them, right behind the mask branch."""
+        placed = trans = 0
+        for i in list(pending):
+            text, lds_name, deps = valu[i]
+            is_trans = text.startswith("v_exp")
+            first_s = after_mask[i] and not masked[0]
+            pad = max(S_HAZARD - ws[0] - 2, 0) if first_s else 0
+            need = 1 + (2 + (pad > 0) if first_s else 0)
+            if placed + need > budget:
+                if first_s:
+                    continue
+                break
+            if is_trans and trans == TRANS_PER_GAP and not last:
+                continue
+            # Within the last gap a chain may run back to back, except where
+            # the hardware does not interlock: a transcendental's result (one
+            # wait state) and a VGPR that v_permlane32_swap reads (two).
+            if not all(d in gap_of and (gap_of[d] < n or (last and not valu[d][0].startswith("v_exp")
+                                                          and not text.startswith("v_permlane")))
+                       for d in deps):
+                continue
+            if first_s:
+                if pad:
+                    emit(f"s_nop {pad - 1}")
+                for t in mask_branch():
+                    emit(t)
+                masked[0] = True
+            elif reads_s[i]:
+                assert ws[0] >= S_HAZARD
+            emit(text, lds_name)
+            gap_of[i] = n
+            pending.remove(i)
+            placed += need
+            trans += is_trans
+
     for m, (kind, idx) in enumerate(mfma):
-        for fr in release.get(m, []):
-            free.append(where[fr])
-        while nxt < len(order) and first_use[order[nxt]] <= m + AHEAD and free:
-            load(order[nxt])
-            nxt += 1
+        for fr in loads_before[m]:
+            load(fr)
         q.wait_for(*needs[m])
         if kind == "qk":
             ks = idx
             a = quad(where[f"K{ks}"])
             b = f"%[q{ks}]" if ks < 32 else quad(where[f"R{ks - 32}"])
             c = "0" if ks == 0 else f"v[{S_BASE}:{S_BASE + 15}]"
-            lines.append(f"v_mfma_f32_32x32x16_bf16 v[{S_BASE}:{S_BASE + 15}], {a}, {b}, {c}")
+            emit(f"v_mfma_f32_32x32x16_bf16 v[{S_BASE}:{S_BASE + 15}], {a}, {b}, {c}")
             if ks < len(stage_qk):
-                lines.extend(stage_qk[ks])
+                for t in stage_qk[ks]:
+                    emit(t)
+            if ks == 35:
+                ws[0] = 0
         else:
             n = idx
             f, rb = n >> 2, n & 3
             o = f"%[o{4 * rb + (f & 3)}]"
-            lines.append(f"v_mfma_f32_32x32x16_bf16 {o}, {quad(where[f'V{f}'])}, "
-                         f"{quad(where[f'P{rb}{f >> 2}'])}, {o}")
-            if n == 0:
-                # The last score op wrote S one value op ago: >= 19 wait
-                # states before the first VALU read of S.
-                lines.append("s_nop 7\\n s_nop 7\\n s_nop 4")
-                lines.extend(mask_branch())
+            emit(f"v_mfma_f32_32x32x16_bf16 {o}, {quad(where[f'V{f}'])}, "
+                 f"{quad(where[f'P{rb}{f >> 2}'])}, {o}")
             if n < len(stage_pv):
-                lines.extend(stage_pv[n])
-            for text, lds_name, _ in per_op[n]:
-                if lds_name:
-                    q.issue(text, lds_name)
-                else:
-                    lines.append(text)
-    assert nxt == len(order)
+                for t in stage_pv[n]:
+                    emit(t)
+            nxt_loads = sum(n_instr(fr) for fr in loads_before[m + 1]) if m + 1 < len(mfma) else 0
+            budget = GAP_BUDGET - nxt_loads - (1 if m + 1 < len(mfma) else 0)
+            last = n == len(mfma) - 37   # the last gap takes whatever is left
+            fill_gap(n, 10 ** 6 if last else max(budget, 1), last)
+    assert not pending, "softmax does not fit between the value ops"
     if STORES_AT_END:
         for h in range(2):
             q.issue(f"ds_write_b128 %[pw], {quad(P_QUADS[h])} offset:{1024 * h}", f"w{h}")
