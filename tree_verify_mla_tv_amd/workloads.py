@@ -222,3 +222,37 @@ def make_accept_inputs(parent: np.ndarray, vocab: int, seed: int, logits_dtype: 
     if logits_dtype == "bf16":
         logits = f32_to_bf16_bits(logits)
     return {"draft": draft, "logits": logits, "depth": depth}
+
+
+# Best-first tree builder at the serving shape: 32 requests, a 32-node draft
+# budget (q_len 33), a block drafter proposing its top 8 tokens at each of 16
+# depths.
+BUILD_DEPTH = 16
+BUILD_TOPK = 8
+
+
+def make_build_inputs(B: int, depth: int, topk: int, seed: int, vocab: int = SERVE_VOCAB,
+                      sort: bool = True, alpha: float = 0.3) -> dict:
+    """Synthetic drafter proposals for the best-first tree builder.
+
+    Recipe: ``numpy.random.default_rng(seed)``.  At each (request, depth) a
+    probability vector over topk + 1 outcomes is drawn from Dirichlet(alpha)
+    (the extra outcome stands for the rest of the vocabulary); the log of the
+    first topk entries in float32 are the candidates' log-probs, sorted
+    descending when ``sort`` (a top-k list), else left in draw order.  Tokens
+    are topk distinct ids drawn uniformly from [0, vocab).  Root tokens are
+    uniform.  Returns logp [B, depth, topk] float32, cand_tok [B, depth, topk]
+    int32, root_tok [B] int32.
+    """
+    rng = np.random.default_rng(seed)
+    pr = rng.dirichlet(np.full(topk + 1, alpha), size=(B, depth))[..., :topk]
+    with np.errstate(divide="ignore"):
+        logp = np.log(pr).astype(np.float32)
+    if sort:
+        logp = -np.sort(-logp, axis=-1)
+    tok = np.empty((B, depth, topk), dtype=np.int32)
+    for b in range(B):
+        for d in range(depth):
+            tok[b, d] = rng.choice(vocab, size=topk, replace=False)
+    root = rng.integers(0, vocab, size=B).astype(np.int32)
+    return {"logp": logp, "cand_tok": tok, "root_tok": root}
