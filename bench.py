@@ -131,9 +131,10 @@ def _time_ms(torch, fn, reps: int) -> float:
 
 
 def next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, with_oracle: bool) -> dict:
-    """The steps after verify on the same batch: the target's greedy token per
-    node over a K2-class vocabulary (fp32 logits), greedy tree accept, and
-    compaction of the accepted rows of the bf16 cache."""
+    """The steps around verify on the same batch: the target's greedy token per
+    node over a K2-class vocabulary (fp32 logits), greedy tree accept,
+    compaction of the accepted rows of the bf16 cache, and (before verify) the
+    best-first tree builder on synthetic drafter proposals."""
     import numpy as np
     dev = c_kv.device
     x = W.make_accept_inputs(inp["parent"], W.SERVE_VOCAB, seed=1234)
@@ -146,6 +147,13 @@ def next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, with_oracle: bool) -> 
     c2, r2 = c_kv.clone(), k_rope.clone()
     ms_compact = _time_ms(torch, lambda: tv.kv_compact(c2, r2, path, n, w.prefix_len), 50)
     n_host = n.cpu().numpy()
+    # The step before verify: best-first trees from synthetic drafter proposals.
+    bx = W.make_build_inputs(w.B, W.BUILD_DEPTH, W.BUILD_TOPK, seed=99)
+    b_lp = torch.from_numpy(bx["logp"]).to(dev)
+    b_tok = torch.from_numpy(bx["cand_tok"]).to(dev)
+    b_root = torch.from_numpy(bx["root_tok"]).to(dev)
+    budget = w.q_len - 1
+    ms_build = _time_ms(torch, lambda: tv.tree_build(b_lp, b_tok, b_root, budget), 50)
     logit_bytes = logits.numel() * 4
     moved_bytes = int(n_host.sum()) * 2 * (w.d_c + w.d_r) * 2
     out = {
@@ -157,6 +165,8 @@ def next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, with_oracle: bool) -> 
                         "bound": "launch latency (integer walk, one wave per tree)"},
         "kv_compact": {"ms": round(ms_compact, 4), "bytes_moved": moved_bytes,
                        "bound": "launch latency (a few hundred KB)"},
+        "tree_build": {"ms": round(ms_build, 4), "budget": budget, "depth": W.BUILD_DEPTH, "topk": W.BUILD_TOPK,
+                       "bound": "launch latency (one wave per request, budget dependent pops)"},
     }
     if with_oracle:
         from oracle import accept_oracle as A
@@ -166,6 +176,10 @@ def next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, with_oracle: bool) -> 
         dt = (time.perf_counter() - t0) * w.B / 4
         out["cpu_oracle_ms"] = {"value": round(dt * 1e3, 1), "sample": "greedy tokens + accept on 4 of 32 trees, "
                                                                        "scaled x8"}
+        from oracle import tree_build_oracle as T
+        t0 = time.perf_counter()
+        T.best_first_tree(bx["logp"], bx["cand_tok"], bx["root_tok"], budget)
+        out["tree_build"]["cpu_oracle_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
     return out
 
 

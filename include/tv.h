@@ -212,6 +212,34 @@ tv_status_t tv_kv_compact(void* c_kv, void* k_rope, tv_dtype_t kv_dtype, const i
                           const int32_t* accept_len, int32_t prefix_len, int32_t B, int32_t kv_len, int32_t q_len,
                           int32_t d_c, int32_t d_r, hipStream_t stream);
 
+/*
+ * tv_tree_build — best-first draft tree per request, the step before verify.
+ *   [Verify page, "The Context: What Led to This Moment" (a GPU best-first
+ *   tree builder in place of a per-request CPU heap); RoPE page, "The Broader
+ *   Context: A Full Native Engine from Scratch" (a drafter proposes candidate
+ *   tokens; the kernels are bit-exact against their reference)]
+ *   The drafter proposes, at each depth d = 1..D, K candidates: token
+ *   cand_tok[b][d-1][c] with log-prob logp[b][d-1][c] (a NaN counts as -inf;
+ *   +inf is outside the contract).  A node is a path of candidates; its score
+ *   is the float32 sum of their log-probs, added from the root down.  Starting
+ *   from the root, budget times the best node whose parent is in the tree
+ *   joins it as the next node: the higher score, then the smaller depth, the
+ *   smaller parent index, the smaller candidate rank (candidates of a depth
+ *   ranked by log-prob, higher first, equal ones by index).  Nodes come out in
+ *   topological order, ready for tv_verify_attn.
+ *   Inputs (device, 4-byte aligned): logp f32 [B][D][K], cand_tok int32
+ *   [B][D][K], root_tok int32 [B].  Only depths 1..min(D, budget) are read.
+ *   Outputs (device, 4-byte aligned), [B][budget + 1] each: parent int32 (-1
+ *   for the root), token int32 (root_tok for the root), depth int32 (0 for the
+ *   root), score f32 (0 for the root); slots past the drafted nodes hold -1, -1,
+ *   -1, -inf.  n_nodes int32 [B]: drafted nodes (budget unless the candidates
+ *   run out: K + K^2 + ... + K^D < budget).
+ *   1 <= K <= 64, D >= 1, 0 <= budget <= TV_MAX_Q_LEN - 1, B >= 1.
+ */
+tv_status_t tv_tree_build(const float* logp, const int32_t* cand_tok, const int32_t* root_tok, int32_t B, int32_t D,
+                          int32_t K, int32_t budget, int32_t* parent, int32_t* token, int32_t* depth, float* score,
+                          int32_t* n_nodes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

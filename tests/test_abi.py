@@ -162,3 +162,18 @@ def test_kv_compact_rejects_before_launch():
     assert f(A, A, 1, A, A, 4, 1, 7, 3, 12, 64, None) == UNS           # 24-byte rows
     assert f(A + 8, A, 1, A, A, 4, 1, 7, 3, 512, 64, None) == INV      # c_kv not 16-byte aligned
     assert f(A, A, 9, A, A, 4, 1, 7, 3, 512, 64, None) == INV          # dtype
+
+
+def test_tree_build_rejects_before_launch():
+    lib = tv.load()
+    f = lib.tv_tree_build
+    args = lambda B=2, D=4, K=8, budget=32, lp=A, out=A: (lp, A, A, B, D, K, budget, out, A, A, A, A, None)
+    assert f(*args(K=0)) == INV
+    assert f(*args(K=65)) == UNS
+    assert f(*args(D=0)) == INV
+    assert f(*args(B=0)) == INV
+    assert f(*args(budget=-1)) == INV
+    assert f(*args(budget=64)) == UNS
+    assert f(*args(lp=None)) == INV
+    assert f(*args(lp=A + 2)) == INV
+    assert f(*args(out=None)) == INV

@@ -148,6 +148,10 @@ hipError_t launch_tree_accept(const int32_t* parent, const int32_t* draft, const
                               int32_t* path, int32_t* accept_len, int32_t* bonus, hipStream_t stream);
 hipError_t launch_kv_compact(void* c_kv, void* k_rope, int elem_bytes, const int32_t* path, const int32_t* accept_len,
                              int prefix_len, int B, int kv_len, int q_len, int d_c, int d_r, hipStream_t stream);
+// The step before verify (tree_build.hip).
+hipError_t launch_tree_build(const float* logp, const int32_t* cand_tok, const int32_t* root_tok, int B, int D, int K,
+                             int budget, int32_t* parent, int32_t* token, int32_t* depth, float* score,
+                             int32_t* n_nodes, hipStream_t stream);
 
 // Kernel launchers (one per kernel family).
 hipError_t launch_attn_valu(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);

@@ -41,6 +41,7 @@ SIGNATURES = {
     "tv_argmax_rows": (_i32, [_p, _i32, _i64, _i32, _p, _p]),
     "tv_tree_accept": (_i32, [_p, _p, _p, _i32, _i32, _p, _p, _p, _p]),
     "tv_kv_compact": (_i32, [_p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
+    "tv_tree_build": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
 }
 
 
@@ -278,3 +279,28 @@ def kv_compact(c_kv: torch.Tensor, k_rope: torch.Tensor, path: torch.Tensor, acc
                                                  _ptr(accept_len), prefix_len, B, kv, q, d_c, k_rope.shape[2],
                                                  _stream()))
     return c_kv, k_rope
+
+
+def tree_build(logp: torch.Tensor, cand_tok: torch.Tensor, root_tok: torch.Tensor, budget: int):
+    """Best-first draft tree per request from the drafter's proposals: logp
+    float32 [B, D, K], cand_tok int32 [B, D, K], root_tok int32 [B].  Returns
+    (parent, token, depth, score) each [B, budget + 1] (int32, int32, int32,
+    float32) and n_nodes [B] int32."""
+    _cuda_contig("logp", logp)
+    _cuda_contig("cand_tok", cand_tok)
+    _cuda_contig("root_tok", root_tok)
+    _need(logp.dtype == torch.float32 and logp.dim() == 3, "logp must be float32 [B, D, K]")
+    _need(cand_tok.dtype == torch.int32 and cand_tok.shape == logp.shape, "cand_tok must be int32 like logp")
+    B, D, K = logp.shape
+    _need(root_tok.dtype == torch.int32 and root_tok.shape == (B,), "root_tok must be int32 [B]")
+    dev = logp.device
+    q = budget + 1
+    parent = torch.empty(B, q, dtype=torch.int32, device=dev)
+    token = torch.empty(B, q, dtype=torch.int32, device=dev)
+    depth = torch.empty(B, q, dtype=torch.int32, device=dev)
+    score = torch.empty(B, q, dtype=torch.float32, device=dev)
+    n_nodes = torch.empty(B, dtype=torch.int32, device=dev)
+    _check("tv_tree_build", load().tv_tree_build(_ptr(logp), _ptr(cand_tok), _ptr(root_tok), B, D, K, budget,
+                                                 _ptr(parent), _ptr(token), _ptr(depth), _ptr(score),
+                                                 _ptr(n_nodes), _stream()))
+    return parent, token, depth, score, n_nodes
