@@ -28,6 +28,30 @@ void cut(int kv_len, int want, int tile, int& n, int& chunk) {
   chunk = ceil_div(chunk, tile) * tile;
   n = ceil_div(kv_len, chunk);
 }
+
+// Splits for `blocks` row blocks over kv_len keys when they alone cannot fill
+// `slots` concurrent workgroups: the count that minimises the launch's time,
+// modelled as rounds of workgroups x (tiles per piece + a unit's fixed set-up
+// in tile-steps); ties go to fewer splits (less merging).  Rounding the count
+// up instead (blocks x splits just above slots) would add a nearly empty
+// second round.
+void cut_for_blocks(int kv_len, long long blocks, long long slots, int tile, int setup_tiles, int& n, int& chunk) {
+  const int max_split = kv_len / kMinKeysPerSplit > 1 ? kv_len / kMinKeysPerSplit : 1;
+  long long best_cost = -1;
+  int best = 1;
+  for (int want = 1; want <= max_split; ++want) {
+    int sn, sc;
+    cut(kv_len, want, tile, sn, sc);
+    if (sn != want) continue;  // an equivalent cut was already counted
+    const long long rounds = (blocks * sn + slots - 1) / slots;
+    const long long cost = rounds * (sc / tile + setup_tiles);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = sn;
+    }
+  }
+  cut(kv_len, best, tile, n, chunk);
+}
 }  // namespace
 
 AttnPlan plan_attention(const AttnShape& s) {
@@ -46,8 +70,9 @@ AttnPlan plan_attention(const AttnShape& s) {
 
   const long long blocks = static_cast<long long>(s.B) * p.n_rb;
   if (blocks < target) {
-    // Too few row blocks: cut every block's kv range.
-    cut(s.kv_len, ceil_div(target, blocks), p.keys_per_tile, p.split_full, p.chunk_full);
+    // Too few row blocks: cut every block's kv range.  A unit's set-up (tree
+    // masks, queries, first tile, output) costs about ten tile-steps.
+    cut_for_blocks(s.kv_len, blocks, target, p.keys_per_tile, 10, p.split_full, p.chunk_full);
     p.split_tail = p.split_full;
     p.chunk_tail = p.chunk_full;
   } else {

@@ -48,8 +48,9 @@ constexpr int kMfmaThreads = 256;
 // are cut into split_full kv ranges of chunk_full rows, the partial last block
 // into split_tail ranges of chunk_tail rows (a short last round of the grid is
 // then filled by short units).  Units of full blocks come first in launch
-// order.  A row block cut into more than one range writes partial results to
-// the workspace ("slots"), combined afterwards by the merge pass.
+// order, ordered by tree, then kv range, then row block.  A row block cut into
+// more than one range writes partial results to the workspace ("slots",
+// numbered by tree, row block, range), combined afterwards by the merge pass.
 struct AttnPlan {
   AttnKernel kernel;
   int rows_per_block;
@@ -100,10 +101,12 @@ __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long long u) {
   const long long units_full = static_cast<long long>(a.B) * a.full_rb * a.split_full;
   int chunk;
   if (u < units_full) {
-    w.split = static_cast<int>(u % a.split_full);
-    const long long t = u / a.split_full;
-    w.rb = static_cast<int>(t % a.full_rb);
-    w.b = static_cast<int>(t / a.full_rb);
+    // Tree, then kv range, then row block: the row blocks reading one kv range
+    // are neighbours in launch order (and so mostly share an XCD's L2).
+    w.rb = static_cast<int>(u % a.full_rb);
+    const long long t = u / a.full_rb;
+    w.split = static_cast<int>(t % a.split_full);
+    w.b = static_cast<int>(t / a.split_full);
     chunk = a.chunk_full;
     w.slot = a.split_full > 1 ? (static_cast<long long>(w.b) * a.full_rb + w.rb) * a.split_full + w.split : -1;
   } else {
