@@ -57,7 +57,7 @@ def _attn(lib, **kw):
     (dict(q_lat=None), INV), (dict(q_rope=None), INV), (dict(c_kv=None), INV), (dict(k_rope=None), INV),
     (dict(parent=None), INV), (dict(out=None), INV),
     (dict(B=0), INV), (dict(H=0), INV), (dict(q=0), INV), (dict(prefix=-1), INV),
-    (dict(q=65), UNS), (dict(d_r=33), INV), (dict(d_c=100), UNS), (dict(d_r=16), UNS), (dict(dt=7), INV),
+    (dict(q=257), UNS), (dict(d_r=33), INV), (dict(d_c=100), UNS), (dict(d_r=16), UNS), (dict(dt=7), INV),
     (dict(q_lat=A + 8), INV), (dict(c_kv=A + 4), INV), (dict(out=A + 12), INV), (dict(parent=A + 2), INV),
     (dict(lse=A + 1), INV), (dict(scale=float("inf")), INV), (dict(scale=float("nan")), INV),
     (dict(prefix=2**31 - 10), INV),
@@ -83,7 +83,7 @@ def test_workspace_size_is_a_function_of_shapes():
     assert f(2, 64, 9, 512, 512, 64, tv.TV_F32) == f(2, 64, 9, 512, 512, 64, tv.TV_F32)
     assert f(1, 1, 1, 5000, 512, 64, tv.TV_F32) > 0
     assert f(0, 1, 1, 10, 512, 64, tv.TV_F32) == 0          # invalid shape -> 0
-    assert f(1, 1, 65, 10, 512, 64, tv.TV_F32) == 0         # unsupported -> 0
+    assert f(1, 1, 257, 10, 512, 64, tv.TV_F32) == 0         # unsupported -> 0
 
 
 def test_rope_rejects_before_launch():
@@ -107,7 +107,7 @@ def test_tree_positions_rejects_before_launch():
     assert lib.tv_tree_positions(None, 1, 3, 0, A, None) == INV
     assert lib.tv_tree_positions(A, 1, 3, 0, None, None) == INV
     assert lib.tv_tree_positions(A, 0, 3, 0, A, None) == INV
-    assert lib.tv_tree_positions(A, 1, 65, 0, A, None) == UNS
+    assert lib.tv_tree_positions(A, 1, 257, 0, A, None) == UNS
     assert lib.tv_tree_positions(A, 1, 3, -2, A, None) == INV
 
 
@@ -115,14 +115,14 @@ def test_verify_step_rejects_before_launch():
     lib = tv.load()
     s = lib.tv_verify_step
     assert s(A, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.0, 0.1, A, None, None, 0, None) == INV   # theta
-    assert s(A, A, A, A, A, 4, 1, 2, 70, 64, 32, 0, 1e4, 0.1, A, None, None, 0, None) == UNS  # q_len
+    assert s(A, A, A, A, A, 4, 1, 2, 257, 64, 32, 0, 1e4, 0.1, A, None, None, 0, None) == UNS  # q_len
     assert s(A, None, A, A, A, 4, 1, 2, 3, 64, 32, 0, 1e4, 0.1, A, None, None, 0, None) == INV
 
 
 def test_tree_rope_rejects_before_launch():
     r = tv.load().tv_tree_rope
     assert r(A, A, 0, A, 4, 1, 2, 3, 64, 0.0, None) == INV      # theta
-    assert r(A, A, 0, A, 4, 1, 2, 65, 64, 1e4, None) == UNS     # q_len
+    assert r(A, A, 0, A, 4, 1, 2, 257, 64, 1e4, None) == UNS     # q_len
     assert r(A, A, 3, A, 4, 1, 2, 3, 64, 1e4, None) == INV      # dtype
     assert r(A, A, 0, A, 4, 1, 2, 3, 63, 1e4, None) == INV      # odd d_r
     assert r(None, A, 0, A, 4, 1, 2, 3, 64, 1e4, None) == INV
@@ -149,7 +149,7 @@ def test_tree_accept_rejects_before_launch():
     assert f(None, A, A, 1, 3, A, A, A, None) == INV
     assert f(A, A, A, 0, 3, A, A, A, None) == INV
     assert f(A, A, A, 1, 0, A, A, A, None) == INV
-    assert f(A, A, A, 1, 65, A, A, A, None) == UNS
+    assert f(A, A, A, 1, 257, A, A, A, None) == UNS
     assert f(A, A, A + 2, 1, 3, A, A, A, None) == INV
     assert f(A, A, A, 1, 3, A, None, A, None) == INV
 
@@ -158,7 +158,7 @@ def test_kv_compact_rejects_before_launch():
     f = tv.load().tv_kv_compact
     assert f(None, A, 1, A, A, 4, 1, 7, 3, 512, 64, None) == INV
     assert f(A, A, 1, A, A, 5, 1, 7, 3, 512, 64, None) == INV          # prefix + q_len > kv_len
-    assert f(A, A, 1, A, A, 4, 1, 7, 65, 512, 64, None) == UNS
+    assert f(A, A, 1, A, A, 4, 1, 7, 257, 512, 64, None) == UNS
     assert f(A, A, 1, A, A, 4, 1, 7, 3, 12, 64, None) == UNS           # 24-byte rows
     assert f(A + 8, A, 1, A, A, 4, 1, 7, 3, 512, 64, None) == INV      # c_kv not 16-byte aligned
     assert f(A, A, 9, A, A, 4, 1, 7, 3, 512, 64, None) == INV          # dtype

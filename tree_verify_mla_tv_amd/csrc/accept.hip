@@ -107,42 +107,61 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const void* __restrict
   }
 }
 
-// One wave per tree: lane i holds node i's parent and draft token.  From the
-// current node cur, the wanted token is target[cur]; the lowest lane whose node
-// is a child of cur carrying that token is accepted (a ballot), until none is.
-// A node whose parent lies outside [0, i) is never a candidate, so such a node
-// is simply never accepted (and the walk takes at most q_len - 1 steps).
+// One wave per tree: lane l holds nodes l + 64 j (j < kMaxQ / 64), with their
+// parents and draft tokens.  From the current node cur, the wanted token is
+// target[cur]; the lowest node that is a child of cur carrying that token is
+// accepted (one ballot per group of 64 nodes, the lowest group first), until
+// none is.  A node whose parent lies outside [0, i) is never a candidate, so
+// such a node is simply never accepted (and the walk takes at most q_len - 1
+// steps).
 __global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* __restrict__ parent,
                                                          const int32_t* __restrict__ draft,
                                                          const int32_t* __restrict__ target, int q_len,
                                                          int32_t* __restrict__ path, int32_t* __restrict__ accept_len,
                                                          int32_t* __restrict__ bonus) {
+  constexpr int kPer = kMaxQ / 64;
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int64_t o = static_cast<int64_t>(b) * q_len;
   __shared__ int32_t s_target[kMaxQ];
-  const bool node = lane < q_len;
-  const int32_t par = node ? parent[o + lane] : -2;
-  const int32_t tok = node ? draft[o + lane] : 0;
-  if (node) s_target[lane] = target[o + lane];
+  int32_t par[kPer], tok[kPer], my_step[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int node = lane + 64 * j;
+    const bool in = node < q_len;
+    par[j] = in ? parent[o + node] : -2;
+    tok[j] = in ? draft[o + node] : 0;
+    my_step[j] = node == 0 ? 0 : -1;  // position of the node on the accepted path
+    if (in) s_target[node] = target[o + node];
+  }
   __syncthreads();
-  int32_t my_step = lane == 0 ? 0 : -1;  // position of this node on the accepted path
   int cur = 0;
   int n = 0;
   for (int depth = 1; depth < q_len; ++depth) {
     const int32_t want = s_target[cur];
-    const bool cand = node && lane > 0 && par == cur && par < lane && tok == want;
-    const unsigned long long m = __ballot(cand);
-    if (m == 0ull) break;
-    const int c = __ffsll(static_cast<long long>(m)) - 1;
-    if (lane == c) my_step = depth;
+    int c = -1;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int node = lane + 64 * j;
+      const bool cand = node < q_len && node > 0 && par[j] == cur && par[j] < node && tok[j] == want;
+      const unsigned long long m = __ballot(cand);
+      if (c < 0 && m != 0ull) c = 64 * j + __ffsll(static_cast<long long>(m)) - 1;
+    }
+    if (c < 0) break;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (lane + 64 * j == c) my_step[j] = depth;
     cur = c;
     n = depth;
   }
   // path[k] = the node whose step is k; -1 past the accepted length.
-  if (node) path[o + lane] = -1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (lane + 64 * j < q_len) path[o + lane + 64 * j] = -1;
   __syncthreads();
-  if (my_step >= 0) path[o + my_step] = lane;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (my_step[j] >= 0) path[o + my_step[j]] = lane + 64 * j;
   if (lane == 0) {
     accept_len[b] = n;
     bonus[b] = s_target[cur];

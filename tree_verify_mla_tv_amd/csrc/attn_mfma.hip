@@ -215,10 +215,11 @@ __device__ __forceinline__ void step(const StepBufs& sb, const TreeKv& kv, const
 
 __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArgs a) {
   __shared__ int s_par[kMaxQ];
-  __shared__ unsigned long long s_anc[kMaxQ];
+  __shared__ unsigned long long s_anc[kMaxQ * kAncWords];
   __shared__ __align__(16) unsigned char s_qrope[kMfmaRows * mf::DR * 2];  // 16 KB
   __shared__ float s_row_l[kMfmaRows];
   __shared__ int s_redo;
+  __shared__ uint16_t s_vis[kMaxBoundaryTiles * kMfmaThreads];  // masks of the boundary tiles, per thread
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -245,7 +246,6 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   const int row = row0 + (lane & 31);
   const bool row_valid = row < a.R;
   const int node = min(row / a.H, a.q_len - 1);
-  const unsigned long long anc = s_anc[node];
 
   // Query fragments: q[row][8 g2 + 16 ks .. + 7] * sm_scale * log2(e) as bf16.
   // Latent part (ks < 32) in registers; rope part in LDS, chunk-major:
@@ -281,6 +281,29 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
     }
   }
   const unsigned char* qrope = s_qrope + (wave * 32 + (lane & 31)) * 16;
+
+  // Visibility of the boundary tiles: the tiles from t_first on hold tree keys
+  // or the range end (kt + 32 > min(P, k_end)); at most q_len / 32 + 2 of
+  // them.  Score i of this thread holds key kt + 8 (i/4) + 4 g2 + i % 4;
+  // bit i of its mask says whether that key is visible from the row's node.
+  const int t_first = max(0, (min(P, w.k_end) - w.k_begin) / kMfmaKeys);
+  {
+    const int n_bt = min(n_tiles - t_first, kMaxBoundaryTiles);
+    for (int j = 0; j < n_bt; ++j) {
+      const int kt = w.k_begin + (t_first + j) * kMfmaKeys;
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kt + 8 * (i >> 2) + 4 * g2 + (i & 3);
+        const int rel = key - P;  // tree node of a tree key
+        const bool v = key < w.k_end &&
+                       (key < P || (static_cast<unsigned>(rel) < static_cast<unsigned>(a.q_len) &&
+                                    anc_bit(s_anc, node, rel)));
+        m |= static_cast<uint32_t>(v) << i;
+      }
+      s_vis[j * kMfmaThreads + threadIdx.x] = static_cast<uint16_t>(m);
+    }
+  }
 
   // o[4 rb + db][i] = O[32 rb + lane % 32][col(db, i)] with (value-operand row
   // 8 (i/4) + 4 g2 + i % 4 = 16 gp + 4 q + e, see step)
@@ -324,17 +347,8 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
         vis = 0;
         nm = 1;
       } else if (kt + kMfmaKeys > P || kt + kMfmaKeys > w.k_end) {
-        // Score i holds key kt + 8 (i/4) + 4 g2 + i % 4.
         nm = 1;
-        vis = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt + 8 * (i >> 2) + 4 * g2 + (i & 3);
-          const int rel = key - P;  // tree node of a tree row; the bit test is valid for 0 <= rel < 64
-          const bool tree_vis = (static_cast<unsigned>(rel) < 64u) & (((anc >> (rel & 63)) & 1ull) != 0ull);
-          const bool v = (key < w.k_end) & ((key < P) | tree_vis);
-          vis |= static_cast<uint32_t>(v) << i;
-        }
+        vis = s_vis[min(t - t_first, kMaxBoundaryTiles - 1) * kMfmaThreads + threadIdx.x];
       }
       const StepBufs sb{kc, t == 0 ? kc : kp, kn, g_p[(t + 1) & 1], g_p[t & 1]};
       step(sb, kv, qf, qrope, o, st, lane, wave, kt, vis, nm);

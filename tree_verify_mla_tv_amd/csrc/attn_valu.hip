@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   __shared__ float sM[kValuRows];
   __shared__ float sL[kValuRows];
   __shared__ int s_par[kMaxQ];
-  __shared__ unsigned long long s_anc[kMaxQ];
+  __shared__ unsigned long long s_anc[kMaxQ * kAncWords];
 
   const int tid = threadIdx.x;
   const Unit w = decode_unit(a, unit_of_block(a, blockIdx.x));
@@ -86,7 +86,6 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   const int sr = tid / 16;
   const int sl = tid % 16;
   const int node = min((r0 + sr) / a.H, a.q_len - 1);
-  const unsigned long long anc = s_anc[node];
   float m_run = -INFINITY;
   float l_run = 0.f;
 
@@ -128,8 +127,9 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
     }
     const int key0 = kt + sl;
     const int key1 = kt + sl + 16;
-    const bool vis0 = key0 < k_end && (key0 < P || ((anc >> (key0 - P)) & 1ull));
-    const bool vis1 = key1 < k_end && (key1 < P || ((anc >> (key1 - P)) & 1ull));
+    // key < k_end <= prefix + q_len, so a tree key's index is below q_len.
+    const bool vis0 = key0 < k_end && (key0 < P || anc_bit(s_anc, node, key0 - P));
+    const bool vis1 = key1 < k_end && (key1 < P || anc_bit(s_anc, node, key1 - P));
     const float s0 = vis0 ? acc0 * a.sm_scale : -INFINITY;
     const float s1 = vis1 ? acc1 * a.sm_scale : -INFINITY;
 

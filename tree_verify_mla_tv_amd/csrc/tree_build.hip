@@ -28,7 +28,8 @@ namespace tv {
 namespace {
 
 constexpr int kBuildMaxK = 64;
-constexpr int kBuildMaxDepth = kMaxQ - 1;  // depths past the budget are never reached
+constexpr int kBuildMaxNodes = 64;                   // root + budget <= 64: one frontier entry per lane
+constexpr int kBuildMaxDepth = kBuildMaxNodes - 1;  // depths past the budget are never reached
 
 // Order-preserving key of a float (larger value -> larger key); -0 and +0 share one.
 __device__ __forceinline__ uint32_t order_key(float x) {
@@ -85,10 +86,10 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float* __restrict_
   __shared__ float s_raw[kBuildMaxDepth * kBuildMaxK];
   __shared__ float s_lp[kBuildMaxDepth][kBuildMaxK];         // log-probs in rank order
   __shared__ unsigned char s_idx[kBuildMaxDepth][kBuildMaxK];  // rank -> candidate index
-  __shared__ int s_par[kMaxQ];
-  __shared__ int s_dep[kMaxQ];
-  __shared__ int s_cand[kMaxQ];  // node -> offset of its candidate in cand_tok[b]
-  __shared__ float s_sc[kMaxQ];
+  __shared__ int s_par[kBuildMaxNodes];
+  __shared__ int s_dep[kBuildMaxNodes];
+  __shared__ int s_cand[kBuildMaxNodes];  // node -> offset of its candidate in cand_tok[b]
+  __shared__ float s_sc[kBuildMaxNodes];
 
   const int b = blockIdx.x;
   const int lane = threadIdx.x;

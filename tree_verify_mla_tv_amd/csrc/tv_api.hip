@@ -234,7 +234,7 @@ tv_status_t tv_tree_build(const float* logp, const int32_t* cand_tok, const int3
                           int32_t K, int32_t budget, int32_t* parent, int32_t* token, int32_t* depth, float* score,
                           int32_t* n_nodes, hipStream_t stream) {
   if (B < 1 || D < 1 || K < 1 || budget < 0) return TV_ERR_INVALID;
-  if (K > 64 || budget > TV_MAX_Q_LEN - 1) return TV_ERR_UNSUPPORTED;
+  if (K > 64 || budget > TV_MAX_BUILD_BUDGET) return TV_ERR_UNSUPPORTED;
   const void* ptrs[] = {logp, cand_tok, root_tok, parent, token, depth, score, n_nodes};
   for (const void* p : ptrs)
     if (!p || (reinterpret_cast<uintptr_t>(p) & 3u)) return TV_ERR_INVALID;

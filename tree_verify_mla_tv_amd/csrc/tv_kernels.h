@@ -9,7 +9,8 @@
 
 namespace tv {
 
-constexpr int kMaxQ = 64;     // one 64-bit ancestor word per tree node
+constexpr int kMaxQ = 256;     // tree nodes per request
+constexpr int kAncWords = kMaxQ / 64;  // 64-bit ancestor words per node
 constexpr int kMaxHalf = 64;  // d_r <= 128
 
 // inv_freq[k] = 1 / theta^(2k/d_r), computed on the host in float64 and passed
@@ -38,6 +39,9 @@ constexpr int kValuThreads = 256;
 constexpr int kMfmaRows = 128;    // 4 waves x 32 query rows
 constexpr int kMfmaKeys = 32;
 constexpr int kMfmaThreads = 256;
+// Tiles of a unit that hold tree keys or the unit's range end: at most
+// q_len / 32 + 2.
+constexpr int kMaxBoundaryTiles = kMaxQ / kMfmaKeys + 2;
 
 // How one tv_verify_attn call is cut into workgroups ("units").  A pure
 // function of the shapes (never of the device), so the workspace size can be
@@ -160,19 +164,30 @@ hipError_t launch_tree_build(const float* logp, const int32_t* cand_tok, const i
 hipError_t launch_attn_valu(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_mfma_bf16(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 
-// Ancestor bit masks of one tree: bit m of s_anc[i] is set iff node m is node i
-// or one of its ancestors.  Thread i walks its own path (<= q_len steps).
-// Ends with a barrier.
+// Ancestor bit masks of one tree: bit m % 64 of word s_anc[i * kAncWords +
+// m / 64] is set iff node m is node i or one of its ancestors (words past the
+// tree's nodes stay 0).  Thread i walks its own path (<= q_len steps: a parent
+// outside [0, i) ends it).  Ends with a barrier.
 __device__ __forceinline__ void build_ancestors(const int32_t* __restrict__ parent_b, int q_len, int* s_par,
                                                 unsigned long long* s_anc) {
   for (int i = threadIdx.x; i < q_len; i += blockDim.x) s_par[i] = clamp_parent(parent_b[i], i);
   __syncthreads();
   for (int i = threadIdx.x; i < q_len; i += blockDim.x) {
-    unsigned long long anc = 1ull << i;
-    for (int n = s_par[i]; n >= 0; n = s_par[n]) anc |= 1ull << n;
-    s_anc[i] = anc;
+    unsigned long long w[kAncWords] = {};
+    for (int n = i; n >= 0; n = s_par[n]) {
+      const unsigned long long bit = 1ull << (n & 63);
+#pragma unroll
+      for (int k = 0; k < kAncWords; ++k) w[k] |= (n >> 6) == k ? bit : 0ull;  // static indices: no scratch
+    }
+#pragma unroll
+    for (int k = 0; k < kAncWords; ++k) s_anc[i * kAncWords + k] = w[k];
   }
   __syncthreads();
+}
+
+// Whether tree key rel (0 <= rel < q_len) is visible from node `node`.
+__device__ __forceinline__ bool anc_bit(const unsigned long long* s_anc, int node, int rel) {
+  return ((s_anc[node * kAncWords + (rel >> 6)] >> (rel & 63)) & 1ull) != 0ull;
 }
 
 }  // namespace tv
