@@ -133,6 +133,58 @@ size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_
                                      int32_t d_r, tv_dtype_t kv_dtype);
 
 /*
+ * tv_verify_attn_ragged — tv_verify_attn for a batch whose requests have their
+ *   own prefix length and tree size.  Each request's result is exactly that
+ *   of tv_verify_attn on it alone [Verify page, "The Context: What Led to This
+ *   Moment" (the tree-verify attention)]; batching requests of different
+ *   lengths in one launch is this library's addition, not a step the pages
+ *   describe.
+ *   Per-request lengths are in DEVICE memory: prefix_len[B], q_len[B] int32,
+ *   with 0 <= q_len[b] <= max_q_len and prefix_len[b] + q_len[b] <= kv_stride
+ *   (lengths outside are clamped into these bounds; q_len 0 means nothing to
+ *   do).  Nodes are packed request after request: request b's nodes start at
+ *   node s_b = q_len[0] + ... + q_len[b-1] in
+ *     q_lat [N][H][d_c], q_rope [N][H][d_r] f32, parent [N] int32 (node
+ *     indices local to the request, as for tv_verify_attn), out [N][H][d_c]
+ *     f32, lse [N][H] f32 (optional), N = sum of q_len (rows past it are not
+ *     touched);
+ *   the cache holds kv_stride rows per request, the first prefix_len[b] +
+ *   q_len[b] of which are used: c_kv [B][kv_stride][d_c], k_rope
+ *   [B][kv_stride][d_r] (kv_dtype), rope slices already rotated.
+ *   Workspace (device, 16-byte aligned, caller-owned, reused across calls on
+ *   one stream): at least tv_verify_attn_ragged_workspace_size(...) bytes; it
+ *   always holds the per-request records a small prep kernel writes from the
+ *   device lengths, then the split partials.  Launch sizes come from the
+ *   bounds, so nothing is read back to the host and the call can be captured
+ *   in a graph.  1 <= max_q_len <= TV_MAX_Q_LEN; kv_stride >= max_q_len;
+ *   other limits as for tv_verify_attn with prefix_len = kv_stride -
+ *   max_q_len.
+ */
+tv_status_t tv_verify_attn_ragged(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
+                                  tv_dtype_t kv_dtype, float sm_scale, float* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tv_verify_step_ragged — the whole step for a ragged batch: each request's
+ *   query rows and tree key rows rotated in place at prefix_len[b] + depth
+ *   (as tv_tree_rope does for one request), then tv_verify_attn_ragged.
+ *   Arguments as for tv_verify_attn_ragged plus theta; q_rope and k_rope are
+ *   modified.  The request records are computed once and serve both steps.
+ */
+tv_status_t tv_verify_step_ragged(const float* q_lat, float* q_rope, const void* c_kv, void* k_rope,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
+                                  tv_dtype_t kv_dtype, double theta, float sm_scale, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes tv_verify_attn_ragged and tv_verify_step_ragged need for
+ * these bounds (0 if the shape is invalid or unsupported). */
+size_t tv_verify_attn_ragged_workspace_size(int32_t B, int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c,
+                                            int32_t d_r, tv_dtype_t kv_dtype);
+
+/*
  * tv_tree_rope — the step's rotation: for every tree b and node i, turn the
  *   query rows q_rope[b,i,h,:] (all heads) and the tree's own key row
  *   k_rope[b, prefix_len+i, :] in place at position prefix_len + depth(i), as

@@ -177,3 +177,30 @@ def test_tree_build_rejects_before_launch():
     assert f(*args(lp=None)) == INV
     assert f(*args(lp=A + 2)) == INV
     assert f(*args(out=None)) == INV
+
+
+def test_verify_attn_ragged_rejects_before_launch():
+    lib = tv.load()
+    ws_size = lib.tv_verify_attn_ragged_workspace_size
+    assert ws_size(3, 8, 33, 9000, 512, 64, 1) > 0
+    assert ws_size(3, 8, 33, 20, 512, 64, 1) == 0        # stride below max_q_len
+    assert ws_size(3, 8, 257, 9000, 512, 64, 1) == 0     # tree too large
+    need = ws_size(3, 8, 33, 9000, 512, 64, 1)
+    f = lib.tv_verify_attn_ragged
+
+    def call(**kw):
+        a = dict(q=A, p=A, B=3, H=8, mq=33, S=9000, d_c=512, d_r=64, dt=1, ws=A, ws_n=need)
+        a.update(kw)
+        return f(a["q"], A, A, A, A, a["p"], A, a["B"], a["H"], a["mq"], a["S"], a["d_c"], a["d_r"], a["dt"], 0.04,
+                 A, None, a["ws"], a["ws_n"], None)
+
+    assert call(S=20) == INV
+    assert call(mq=257) == UNS
+    assert call(B=0) == INV
+    assert call(q=None) == INV
+    assert call(p=None) == INV
+    assert call(p=A + 2) == INV
+    assert call(ws=None) == INV
+    assert call(ws_n=need - 1) == INV
+    assert call(ws=A + 8) == INV
+    assert call(d_c=100) == UNS

@@ -1,0 +1,148 @@
+"""Ragged batches (tv_verify_attn_ragged): requests with their own prefix length
+and tree size in one launch, lengths in device memory.  Each request's rows are
+compared with the float64 oracle run on that request alone."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tv_oracle as O
+from tree_verify_mla_tv_amd import tv
+from tree_verify_mla_tv_amd import workloads as W
+from tvcompare import errors
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max_abs=1e-5, max_rel=1e-2), "bf16": dict(max_rel=2e-2)}
+
+
+def _ragged_inputs(q_lens, prefixes, H, d_c, d_r, dt, stride_pad, seed):
+    rng = np.random.default_rng(seed)
+    B = len(q_lens)
+    S = max(p + q for p, q in zip(prefixes, q_lens)) + stride_pad
+    N = sum(q_lens)
+    scale = 0.5 if dt == "bf16" else 1.0
+    q_lat = (rng.standard_normal((N, H, d_c), dtype=np.float32) * scale).astype(np.float32)
+    q_rope = (rng.standard_normal((N, H, d_r), dtype=np.float32) * scale).astype(np.float32)
+    c_kv = (rng.standard_normal((B, S, d_c), dtype=np.float32) * scale).astype(np.float32)
+    k_rope = (rng.standard_normal((B, S, d_r), dtype=np.float32) * scale).astype(np.float32)
+    if dt == "bf16":
+        c_kv, k_rope = W.f32_to_bf16_bits(c_kv), W.f32_to_bf16_bits(k_rope)
+    trees = ["rrt", "chain", "wide", "branch4"]
+    parent = np.concatenate([W.TREES[trees[b % 4]](q, rng) for b, q in enumerate(q_lens) if q > 0] or
+                            [np.zeros(0, np.int64)]).astype(np.int32)
+    return q_lat, q_rope, c_kv, k_rope, parent
+
+
+def _cache(a, dt):
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _check(q_lens, prefixes, H, d_c, d_r, dt, max_q=None, stride_pad=0):
+    tag = f"ragged q={q_lens} P={prefixes} H={H} d_c={d_c} {dt}"
+    print(tag, flush=True)
+    max_q = max_q or max(max(q_lens), 1)
+    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs(q_lens, prefixes, H, d_c, d_r, dt, stride_pad,
+                                                         seed=zlib.crc32(tag.encode()))
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    out, lse = tv.verify_attn_ragged(torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(),
+                                     _cache(c_kv, dt), _cache(k_rope, dt), torch.from_numpy(parent).cuda(),
+                                     torch.tensor(prefixes, dtype=torch.int32).cuda(),
+                                     torch.tensor(q_lens, dtype=torch.int32).cuda(), max_q, sm, return_lse=True)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    s = 0
+    for b, (q, P) in enumerate(zip(q_lens, prefixes)):
+        if q == 0:
+            continue
+        kv = P + q
+        ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat[None, s:s + q], "f32"), O.as_f64(q_rope[None, s:s + q], "f32"),
+                                         O.as_f64(c_kv[b:b + 1, :kv], dt), O.as_f64(k_rope[b:b + 1, :kv], dt),
+                                         parent[None, s:s + q], P, sm)
+        e = errors(out[s:s + q], ref_out[0])
+        assert e["max_rel"] <= TOL[dt]["max_rel"], (tag, b, e)
+        if "max_abs" in TOL[dt]:
+            assert e["max_abs"] <= TOL[dt]["max_abs"], (tag, b, e)
+        assert np.abs(lse[s:s + q] - ref_lse[0]).max() <= (2e-5 if dt == "f32" else 2.0 ** -7), (tag, b)
+        s += q
+
+
+CASES = [
+    # q_len per request, prefix per request, H, d_c, d_r, dtype
+    ([5, 33, 1, 64, 17], [100, 0, 3000, 511, 8192], 8, 512, 64, "bf16"),
+    ([0, 9, 0, 33], [50, 200, 0, 1000], 16, 512, 64, "bf16"),       # empty requests
+    ([33, 33], [100000, 100], 16, 512, 64, "bf16"),                   # one long request: its own kv pieces
+    ([1, 7, 65, 200], [0, 40, 129, 5], 3, 64, 32, "f32"),             # VALU kernel, multi-word trees
+    ([130, 2, 256], [7000, 1, 300], 2, 512, 64, "f32"),
+    ([3, 1], [0, 0], 1, 128, 64, "bf16"),                              # no prefix at all
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_ragged(case):
+    _check(*case)
+
+
+def test_ragged_many_requests():
+    rng = np.random.default_rng(8)
+    B = 40
+    q_lens = [int(x) for x in rng.integers(0, 65, size=B)]
+    prefixes = [int(x) for x in rng.integers(0, 4000, size=B)]
+    _check(q_lens, prefixes, 16, 512, 64, "bf16", stride_pad=17)
+
+
+def test_ragged_bound_above_lengths():
+    """max_q_len and the cache stride above every request's use."""
+    _check([9, 20], [300, 64], 8, 512, 64, "bf16", max_q=200, stride_pad=5000)
+
+
+def test_ragged_equal_lengths_match_uniform():
+    """Every request the same size: the ragged call agrees with tv_verify_attn
+    to within rounding (its kv pieces may differ)."""
+    B, q, P, H = 3, 17, 700, 8
+    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs([q] * B, [P] * B, H, 512, 64, "bf16", 0, seed=9)
+    sm = 0.0417
+    args = [torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(), _cache(c_kv, "bf16"),
+            _cache(k_rope, "bf16")]
+    r = tv.verify_attn_ragged(*args, torch.from_numpy(parent).cuda(), torch.full((B,), P, dtype=torch.int32).cuda(),
+                              torch.full((B,), q, dtype=torch.int32).cuda(), q, sm)
+    u = tv.verify_attn(args[0].view(B, q, H, 512), args[1].view(B, q, H, 64), args[2], args[3],
+                       torch.from_numpy(parent.reshape(B, q)).cuda(), P, sm)
+    torch.cuda.synchronize()
+    e = errors(r.cpu().numpy().reshape(B, q, H, 512), u.cpu().numpy())
+    assert e["max_rel"] <= 1e-5, e
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_ragged_step(dt):
+    """RoPE at prefix_len[b] + depth for each request, then the attention,
+    against the oracle's whole step on each request alone."""
+    q_lens, prefixes, H = [17, 0, 33, 5, 70], [300, 10, 4096, 0, 1000], 4
+    d_c, d_r = (512, 64) if dt == "bf16" else (128, 32)
+    theta = 10000.0
+    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs(q_lens, prefixes, H, d_c, d_r, dt, 7, seed=31)
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    kr = _cache(k_rope, dt)
+    for b, P in enumerate(prefixes):  # the cache's prefix rows were rotated when written
+        if P:
+            tv.rope_neox(kr[b:b + 1, :P, :], None, theta)
+    qr = torch.from_numpy(q_rope).cuda()
+    out, lse = tv.verify_step_ragged(torch.from_numpy(q_lat).cuda(), qr, _cache(c_kv, dt), kr,
+                                     torch.from_numpy(parent).cuda(), torch.tensor(prefixes, dtype=torch.int32).cuda(),
+                                     torch.tensor(q_lens, dtype=torch.int32).cuda(), max(q_lens), theta, sm,
+                                     return_lse=True)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    s = 0
+    for b, (q, P) in enumerate(zip(q_lens, prefixes)):
+        if q == 0:
+            continue
+        kv = P + q
+        ref = O.verify_step(q_lat[None, s:s + q], q_rope[None, s:s + q], c_kv[b:b + 1, :kv], k_rope[b:b + 1, :kv],
+                            parent[None, s:s + q], P, theta, sm, dt)
+        e = errors(out[s:s + q], ref["out"][0])
+        assert e["max_rel"] <= TOL[dt]["max_rel"], (b, e)
+        s += q

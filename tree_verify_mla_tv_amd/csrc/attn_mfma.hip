@@ -224,28 +224,32 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g2 = lane >> 5;
-  const Unit w = decode_unit(a, unit_of_block(a, blockIdx.x));
-  const int b = w.b;
-  const int P = a.prefix_len;
+  Unit w;
+  if (a.req) {
+    if (!decode_unit_ragged(a, blockIdx.x, w)) return;  // past the batch's units (whole workgroup)
+  } else {
+    w = decode_unit(a, unit_of_block(a, blockIdx.x));
+  }
+  const int P = w.P;
   // Raw buffers over this tree's rows (the host keeps kv_len * 1024 below
   // 2^31, so every offset fits in 32 bits).
   TreeKv kv;
-  kv.lat = raw_buffer(static_cast<const uint16_t*>(a.c_kv) + static_cast<int64_t>(b) * a.kv_len * mf::DC,
-                      static_cast<uint32_t>(a.kv_len) * (mf::DC * 2));
-  kv.rope = raw_buffer(static_cast<const uint16_t*>(a.k_rope) + static_cast<int64_t>(b) * a.kv_len * mf::DR,
-                       static_cast<uint32_t>(a.kv_len) * (mf::DR * 2));
+  kv.lat = raw_buffer(static_cast<const uint16_t*>(a.c_kv) + w.kv_row0 * mf::DC,
+                      static_cast<uint32_t>(w.kv_len) * (mf::DC * 2));
+  kv.rope = raw_buffer(static_cast<const uint16_t*>(a.k_rope) + w.kv_row0 * mf::DR,
+                       static_cast<uint32_t>(w.kv_len) * (mf::DR * 2));
   kv.lane16 = lane * 16;
   kv.kmax = w.k_end - 1;
 
   const int n_tiles = (w.k_end - w.k_begin + kMfmaKeys - 1) / kMfmaKeys;
 
-  build_ancestors(a.parent + static_cast<int64_t>(b) * a.q_len, a.q_len, s_par, s_anc);
+  build_ancestors(a.parent + w.par0, w.q_len, s_par, s_anc);
 
   // This wave's own rows (row block rb = wave).
   const int row0 = w.rb * kMfmaRows + wave * 32;
   const int row = row0 + (lane & 31);
-  const bool row_valid = row < a.R;
-  const int node = min(row / a.H, a.q_len - 1);
+  const bool row_valid = row < w.R;
+  const int node = min(row / a.H, w.q_len - 1);
 
   // Query fragments: q[row][8 g2 + 16 ks .. + 7] * sm_scale * log2(e) as bf16.
   // Latent part (ks < 32) in registers; rope part in LDS, chunk-major:
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   bf16x8_t qf[mf::KSTEPS_LAT];
   {
     const float sc = a.sm_scale * mf::kLog2e;
-    const int64_t grow = static_cast<int64_t>(b) * a.R + (row_valid ? row : 0);
+    const int64_t grow = w.row0 + (row_valid ? row : 0);
     const float* ql = a.q_lat + grow * mf::DC + 8 * g2;
     const float* qr = a.q_rope + grow * mf::DR + 8 * g2;
     const float z = row_valid ? sc : 0.f;
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
         const int key = kt + 8 * (i >> 2) + 4 * g2 + (i & 3);
         const int rel = key - P;  // tree node of a tree key
         const bool v = key < w.k_end &&
-                       (key < P || (static_cast<unsigned>(rel) < static_cast<unsigned>(a.q_len) &&
+                       (key < P || (static_cast<unsigned>(rel) < static_cast<unsigned>(w.q_len) &&
                                     anc_bit(s_anc, node, rel)));
         m |= static_cast<uint32_t>(v) << i;
       }
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   // Row sums of the wave's own rows, for all four waves.
   const float l_tot = sum_halves(st.l);
   if (g2 == 0) s_row_l[wave * 32 + lane] = l_tot;
-  const int64_t tree_row0 = static_cast<int64_t>(b) * a.R;
+  const int64_t tree_row0 = w.row0;
   if (g2 == 0 && row_valid) {
     if (w.slot < 0) {
       if (a.lse) a.lse[tree_row0 + row] = (st.m_ref + log2f(l_tot)) * mf::kLn2;
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
     for (int pass = 0; pass < 16; ++pass) {
       const int rr = 2 * pass + (threadIdx.x >> 7);  // row within the block
       const int r = w.rb * kMfmaRows + rb * 32 + rr;
-      if (r < a.R) {
+      if (r < w.R) {
         const float4 v = *reinterpret_cast<const float4*>((rr < 16 ? g_k0 : g_k1) + (rr & 15) * kOutPitch + c16 * 16);
         float* dst = w.slot < 0 ? a.out + (tree_row0 + r) * mf::DC
                                 : a.ws_o + (w.slot * kMfmaRows + rb * 32 + rr) * mf::DC;

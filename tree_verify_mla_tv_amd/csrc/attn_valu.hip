@@ -56,14 +56,18 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   __shared__ unsigned long long s_anc[kMaxQ * kAncWords];
 
   const int tid = threadIdx.x;
-  const Unit w = decode_unit(a, unit_of_block(a, blockIdx.x));
-  const int b = w.b;
+  Unit w;
+  if (a.req) {
+    if (!decode_unit_ragged(a, blockIdx.x, w)) return;  // past the batch's units (whole workgroup)
+  } else {
+    w = decode_unit(a, unit_of_block(a, blockIdx.x));
+  }
   const int r0 = w.rb * kValuRows;
   const int k_begin = w.k_begin;
   const int k_end = w.k_end;
-  const int P = a.prefix_len;
+  const int P = w.P;
 
-  build_ancestors(a.parent + static_cast<int64_t>(b) * a.q_len, a.q_len, s_par, s_anc);
+  build_ancestors(a.parent + w.par0, w.q_len, s_par, s_anc);
 
   // Query rows: [q_lat | q_rope], zero past the last row.
   for (int idx = tid; idx < kValuRows * C4; idx += kValuThreads) {
@@ -71,8 +75,8 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
     const int c4 = idx - r * C4;
     const int row = r0 + r;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < a.R) {
-      const int64_t grow = static_cast<int64_t>(b) * a.R + row;
+    if (row < w.R) {
+      const int64_t grow = w.row0 + row;
       if (c4 < DC / 4)
         v = *reinterpret_cast<const float4*>(a.q_lat + grow * DC + c4 * 4);
       else
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   // Score-phase role: 16 lanes per row, each lane two keys (sl, sl + 16).
   const int sr = tid / 16;
   const int sl = tid % 16;
-  const int node = min((r0 + sr) / a.H, a.q_len - 1);
+  const int node = min((r0 + sr) / a.H, w.q_len - 1);
   float m_run = -INFINITY;
   float l_run = 0.f;
 
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
       const int key = kt + j;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (key < k_end) {
-        const int64_t krow = static_cast<int64_t>(b) * a.kv_len + key;
+        const int64_t krow = w.kv_row0 + key;
         if (c4 < DC / 4)
           v = load4<KV>(a.c_kv, krow * DC + c4 * 4);
         else
@@ -184,12 +188,12 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   for (int i = 0; i < RPT; ++i) {
     const int r = rg * RPT + i;
     const int row = r0 + r;
-    if (row >= a.R) continue;
+    if (row >= w.R) continue;
     const float l = sL[r];
     const float m = sM[r];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float4 v = make_float4(o[i].x * inv, o[i].y * inv, o[i].z * inv, o[i].w * inv);
-    const int64_t grow = static_cast<int64_t>(b) * a.R + row;
+    const int64_t grow = w.row0 + row;
     if (w.slot < 0) {
       *reinterpret_cast<float4*>(a.out + grow * DC + col4 * 4) = v;
       if (col4 == 0 && a.lse) a.lse[grow] = m + logf(l);

@@ -76,15 +76,26 @@ __global__ __launch_bounds__(64) void tree_positions_kernel(const int32_t* __res
 // The step's rotation: for tree b (blockIdx.y), every query row q_rope[b,i,h,:]
 // and the tree's own key row k_rope[b, prefix+i, :] turn at prefix + depth(i).
 // blockIdx.x strides over the (node, head-or-key, pair) triples of the tree.
+// A ragged batch (req non-null) takes each request's node range, node count
+// and prefix from its record; its query rows are packed request after request
+// and its key rows start at b * kv_len (kv_len = the cache stride).
 template <typename KV>
 __global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_rope,
                                                         typename KV::storage* __restrict__ k_rope,
                                                         const int32_t* __restrict__ parent, int q_len, int H,
-                                                        int half, int prefix_len, int kv_len, RopeFreq f) {
+                                                        int half, int prefix_len, int kv_len, RopeFreq f,
+                                                        const int32_t* __restrict__ req) {
   __shared__ int s_parent[kMaxQ];
   __shared__ int s_depth[kMaxQ];
   const int b = blockIdx.y;
-  tree_depths_lds(parent + static_cast<int64_t>(b) * q_len, q_len, s_parent, s_depth);
+  int64_t node0 = static_cast<int64_t>(b) * q_len;
+  if (req) {
+    const int32_t* r = req + b * kReqFields;
+    node0 = r[kReqQStart];
+    q_len = r[kReqQLen];
+    prefix_len = r[kReqPrefix];
+  }
+  tree_depths_lds(parent + node0, q_len, s_parent, s_depth);
   const int per_node = (H + 1) * half;
   const int total = q_len * per_node;
   for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
@@ -95,7 +106,7 @@ __global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_ro
     const double ang = static_cast<double>(prefix_len + s_depth[i]) * f.inv_freq[k];
     double y1, y2;
     if (h < H) {
-      float* row = q_rope + ((static_cast<int64_t>(b) * q_len + i) * H + h) * 2 * half;
+      float* row = q_rope + ((node0 + i) * H + h) * 2 * half;
       rotate_pair_f64(static_cast<double>(row[k]), static_cast<double>(row[k + half]), ang, y1, y2);
       row[k] = static_cast<float>(y1);
       row[k + half] = static_cast<float>(y2);
@@ -143,10 +154,26 @@ hipError_t launch_tree_rope(float* q_rope, void* k_rope, bool bf16, const int32_
   const int kv_len = prefix_len + q_len;
   if (bf16)
     tree_rope_kernel<BF16><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, q_len,
-                                                                 H, half, prefix_len, kv_len, f);
+                                                                 H, half, prefix_len, kv_len, f, nullptr);
   else
     tree_rope_kernel<F32><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, q_len, H,
-                                                                half, prefix_len, kv_len, f);
+                                                                half, prefix_len, kv_len, f, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_rope_ragged(float* q_rope, void* k_rope, bool bf16, const int32_t* parent, const int32_t* req,
+                                   int B, int max_q, int H, int d_r, int kv_stride, const RopeFreq& f,
+                                   hipStream_t stream) {
+  const int half = d_r / 2;
+  const int total = max_q * (H + 1) * half;
+  const int threads = 256;
+  const int bx = (total + threads - 1) / threads;
+  if (bf16)
+    tree_rope_kernel<BF16><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, max_q,
+                                                                 H, half, 0, kv_stride, f, req);
+  else
+    tree_rope_kernel<F32><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, max_q, H,
+                                                                half, 0, kv_stride, f, req);
   return hipGetLastError();
 }
 

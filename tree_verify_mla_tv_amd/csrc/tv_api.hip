@@ -83,9 +83,116 @@ tv_status_t run_attention(const float* q_lat, const float* q_rope, const void* c
   return tv::launch_attention(s, plan, a, stream) == hipSuccess ? TV_OK : TV_ERR_LAUNCH;
 }
 
+// Shape checks and plan of a ragged batch (bounds max_q_len, kv_stride).
+tv_status_t plan_ragged(int32_t B, int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
+                        tv_dtype_t kv_dtype, tv::AttnShape& s, tv::AttnPlan& plan) {
+  if (kv_stride < max_q_len) return TV_ERR_INVALID;
+  const tv_status_t st = check_attn_shape(kv_stride - max_q_len, B, H, max_q_len, d_c, d_r, kv_dtype);
+  if (st != TV_OK) return st;
+  s = make_shape(kv_stride - max_q_len, B, H, max_q_len, d_c, d_r, kv_dtype);
+  plan = tv::plan_attention_ragged(s);
+  // Unit, slot and row counts are int32 on the device.
+  if (plan.units > INT32_MAX || static_cast<int64_t>(B) * max_q_len * H > INT32_MAX) return TV_ERR_UNSUPPORTED;
+  return TV_OK;
+}
+
+// Checks and kernel arguments of a ragged call (tv_verify_attn_ragged,
+// tv_verify_step_ragged).
+tv_status_t ragged_args(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                        const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B, int32_t H,
+                        int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype,
+                        float sm_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                        tv::AttnShape& s, tv::AttnPlan& plan, tv::AttnArgs& a) {
+  const tv_status_t st = plan_ragged(B, H, max_q_len, kv_stride, d_c, d_r, kv_dtype, s, plan);
+  if (st != TV_OK) return st;
+  if (!q_lat || !q_rope || !c_kv || !k_rope || !parent || !prefix_len || !q_len || !out) return TV_ERR_INVALID;
+  if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(parent) & 3u) || (reinterpret_cast<uintptr_t>(prefix_len) & 3u) ||
+      (reinterpret_cast<uintptr_t>(q_len) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return TV_ERR_INVALID;
+  if (!isfinite(sm_scale)) return TV_ERR_INVALID;
+  if (workspace_bytes < plan.ws_bytes || workspace == nullptr || !aligned16(workspace)) return TV_ERR_INVALID;
+  char* ws = static_cast<char*>(workspace);
+  a = tv::AttnArgs{};
+  a.q_lat = q_lat;
+  a.q_rope = q_rope;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.parent = parent;
+  a.out = out;
+  a.lse = lse;
+  a.req = reinterpret_cast<const int32_t*>(ws);
+  a.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
+  a.ws_m = reinterpret_cast<float*>(ws + plan.ws_m_off);
+  a.ws_l = reinterpret_cast<float*>(ws + plan.ws_l_off);
+  a.B = B;
+  a.H = H;
+  a.q_len = max_q_len;
+  a.prefix_len = kv_stride - max_q_len;
+  a.kv_len = kv_stride;
+  a.R = max_q_len * H;
+  a.rows_per_block = plan.rows_per_block;
+  a.n_rb = plan.n_rb;
+  a.full_rb = plan.full_rb;
+  a.split_full = plan.split_full;
+  a.chunk_full = plan.chunk_full;
+  a.split_tail = plan.split_tail;
+  a.chunk_tail = plan.chunk_tail;
+  a.sm_scale = sm_scale;
+  a.kv_stride = kv_stride;
+  a.chunk = plan.chunk_full;
+  return TV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t tv_verify_attn_ragged_workspace_size(int32_t B, int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c,
+                                            int32_t d_r, tv_dtype_t kv_dtype) {
+  tv::AttnShape s;
+  tv::AttnPlan plan;
+  if (plan_ragged(B, H, max_q_len, kv_stride, d_c, d_r, kv_dtype, s, plan) != TV_OK) return 0;
+  return plan.ws_bytes;
+}
+
+tv_status_t tv_verify_attn_ragged(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
+                                  tv_dtype_t kv_dtype, float sm_scale, float* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  tv::AttnShape s;
+  tv::AttnPlan plan;
+  tv::AttnArgs a;
+  const tv_status_t st = ragged_args(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, B, H, max_q_len,
+                                     kv_stride, d_c, d_r, kv_dtype, sm_scale, out, lse, workspace, workspace_bytes, s,
+                                     plan, a);
+  if (st != TV_OK) return st;
+  if (tv::launch_ragged_prep(s, plan, a, prefix_len, q_len, stream) != hipSuccess) return TV_ERR_LAUNCH;
+  return tv::launch_attention(s, plan, a, stream) == hipSuccess ? TV_OK : TV_ERR_LAUNCH;
+}
+
+tv_status_t tv_verify_step_ragged(const float* q_lat, float* q_rope, const void* c_kv, void* k_rope,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
+                                  tv_dtype_t kv_dtype, double theta, float sm_scale, float* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!(theta > 0.0) || !isfinite(theta)) return TV_ERR_INVALID;
+  if (d_r > 2 * tv::kMaxHalf) return TV_ERR_UNSUPPORTED;
+  tv::AttnShape s;
+  tv::AttnPlan plan;
+  tv::AttnArgs a;
+  const tv_status_t st = ragged_args(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, B, H, max_q_len,
+                                     kv_stride, d_c, d_r, kv_dtype, sm_scale, out, lse, workspace, workspace_bytes, s,
+                                     plan, a);
+  if (st != TV_OK) return st;
+  if (tv::launch_ragged_prep(s, plan, a, prefix_len, q_len, stream) != hipSuccess) return TV_ERR_LAUNCH;
+  const tv::RopeFreq f = make_freq(d_r, theta);
+  if (tv::launch_tree_rope_ragged(q_rope, k_rope, kv_dtype == TV_BF16, parent, a.req, B, max_q_len, H, d_r,
+                                  kv_stride, f, stream) != hipSuccess)
+    return TV_ERR_LAUNCH;
+  return tv::launch_attention(s, plan, a, stream) == hipSuccess ? TV_OK : TV_ERR_LAUNCH;
+}
 
 const char* tv_status_str(tv_status_t s) {
   switch (s) {

@@ -26,6 +26,11 @@ hipError_t launch_tree_positions(const int32_t* parent, int B, int q_len, int pr
                                  hipStream_t stream);
 hipError_t launch_tree_rope(float* q_rope, void* k_rope, bool bf16, const int32_t* parent, int B, int q_len, int H,
                             int d_r, int prefix_len, const RopeFreq& f, hipStream_t stream);
+// The same for a ragged batch, from the request records the prep kernel wrote
+// (launch_ragged_prep).
+hipError_t launch_tree_rope_ragged(float* q_rope, void* k_rope, bool bf16, const int32_t* parent, const int32_t* req,
+                                   int B, int max_q, int H, int d_r, int kv_stride, const RopeFreq& f,
+                                   hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Attention
@@ -76,6 +81,8 @@ struct AttnShape {
 };
 
 AttnPlan plan_attention(const AttnShape& s);
+// Ragged batch: s.q_len is the bound max_q_len and s.kv_len the cache stride.
+AttnPlan plan_attention_ragged(const AttnShape& s);
 
 struct AttnArgs {
   const float* q_lat;
@@ -91,13 +98,36 @@ struct AttnArgs {
   int B, H, q_len, prefix_len, kv_len, R;
   int rows_per_block, n_rb, full_rb, split_full, chunk_full, split_tail, chunk_tail;
   float sm_scale;
+  // Ragged batches (per-request lengths, on the device): req points at the
+  // request records the prep kernel wrote (null for a uniform batch).
+  const int32_t* req;
+  int kv_stride;  // cache rows per request
+  int chunk;      // keys per kv piece
 };
 
-// The work of one unit (one workgroup).
+// Request record of a ragged batch: [B][kReqFields] int32, then the totals
+// (units, merge blocks).
+enum ReqField : int {
+  kReqQStart = 0,  // first node of the request in the packed node arrays
+  kReqQLen,        // nodes (0 .. max_q_len)
+  kReqPrefix,      // prefix rows
+  kReqNRb,         // row blocks
+  kReqSplit,       // kv pieces per row block
+  kReqUnit0,       // first unit
+  kReqSlot0,       // first partial-result slot (when split > 1)
+  kReqMerge0,      // first merged row block (when split > 1)
+  kReqFields
+};
+
+// The work of one unit (one workgroup), with the shape of its request.
 struct Unit {
   int b, rb, split;
   int k_begin, k_end;
   long long slot;  // partial-result slot, or -1 when the row block is not split
+  int q_len, P, R, kv_len;
+  long long row0;     // packed (node, head) row of the request's node 0
+  long long par0;     // offset of the request's parent array
+  long long kv_row0;  // first cache row of the request
 };
 
 __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long long u) {
@@ -124,7 +154,60 @@ __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long long u) {
   }
   w.k_begin = w.split * chunk;
   w.k_end = min(a.kv_len, w.k_begin + chunk);
+  w.q_len = a.q_len;
+  w.P = a.prefix_len;
+  w.R = a.R;
+  w.kv_len = a.kv_len;
+  w.row0 = static_cast<long long>(w.b) * a.R;
+  w.par0 = static_cast<long long>(w.b) * a.q_len;
+  w.kv_row0 = static_cast<long long>(w.b) * a.kv_len;
   return w;
+}
+
+// Last request whose first entry in column `field` is <= v (requests with
+// nothing to do share that entry with the next one, so the search lands on the
+// request that owns v).
+__device__ __forceinline__ int find_request(const int32_t* rq, int B, int field, long long v) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rq[mid * kReqFields + field] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Ragged batch: block x of the launch (an upper bound of units) -> its unit,
+// or false past the batch's real total.  Units are numbered request by
+// request, then kv range, then row block; the first multiple of 8 of the
+// real total is dealt XCD by XCD as for a uniform batch.
+__device__ __forceinline__ bool decode_unit_ragged(const AttnArgs& a, long long x, Unit& w) {
+  const int32_t* rq = a.req;
+  const long long total = rq[a.B * kReqFields];
+  if (x >= total) return false;
+  constexpr int kXcds = 8;
+  const long long f8 = total / kXcds * kXcds;
+  const long long u = x < f8 ? (x % kXcds) * (f8 / kXcds) + x / kXcds : x;
+  const int b = find_request(rq, a.B, kReqUnit0, u);
+  const int32_t* r = rq + b * kReqFields;
+  const int local = static_cast<int>(u - r[kReqUnit0]);
+  const int n_rb = r[kReqNRb];
+  const int n_split = r[kReqSplit];
+  w.b = b;
+  w.rb = local % n_rb;
+  w.split = local / n_rb;
+  w.q_len = r[kReqQLen];
+  w.P = r[kReqPrefix];
+  w.R = w.q_len * a.H;
+  w.kv_len = w.P + w.q_len;
+  w.k_begin = w.split * a.chunk;
+  w.k_end = min(w.kv_len, w.k_begin + a.chunk);
+  w.slot = n_split > 1 ? static_cast<long long>(r[kReqSlot0]) + static_cast<long long>(w.rb) * n_split + w.split
+                       : -1;
+  w.row0 = static_cast<long long>(r[kReqQStart]) * a.H;
+  w.par0 = r[kReqQStart];
+  w.kv_row0 = static_cast<long long>(b) * a.kv_stride;
+  return true;
 }
 
 // Workgroup x of a launch runs on XCD x % 8 (the hardware deals workgroups to
@@ -147,6 +230,10 @@ __device__ __forceinline__ long long unit_of_block(const AttnArgs& a, long long 
 }
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+// Request records of a ragged batch (lengths prefix_len[B], q_len[B] in device
+// memory) into a.req; then launch_attention runs the batch.
+hipError_t launch_ragged_prep(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, const int32_t* prefix_len,
+                              const int32_t* q_len, hipStream_t stream);
 
 // The steps after verify (accept.hip).
 hipError_t launch_argmax_rows(const void* logits, bool bf16, bool vec, int64_t n_rows, int vocab, int32_t* out,

@@ -43,6 +43,11 @@ SIGNATURES = {
     "tv_tree_accept": (_i32, [_p, _p, _p, _i32, _i32, _p, _p, _p, _p]),
     "tv_kv_compact": (_i32, [_p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "tv_tree_build": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "tv_verify_attn_ragged": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                     _p, _p, _p, _sz, _p]),
+    "tv_verify_attn_ragged_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "tv_verify_step_ragged": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f64,
+                                     _f32, _p, _p, _p, _sz, _p]),
 }
 
 
@@ -197,6 +202,64 @@ def verify_attn(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, sm_scale: 
         _ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
         float(sm_scale), _ptr(out), _ptr(lse_t), _ptr(workspace), ws_n, _stream()))
     return (out, lse_t) if (return_lse or lse is not None) else out
+
+
+def verify_attn_ragged(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, max_q_len: int,
+                       sm_scale: float | None = None, out=None, lse=None, return_lse: bool = False, workspace=None):
+    """Tree-verify attention over requests of different lengths (rope slices
+    already rotated).  Nodes packed request after request: q_lat [N, H, d_c],
+    q_rope [N, H, d_r], parent [N] int32 (local node indices); cache c_kv
+    [B, kv_stride, d_c], k_rope [B, kv_stride, d_r]; prefix_len and q_len: int32
+    [B] device tensors (q_len[b] <= max_q_len, prefix_len[b] + q_len[b] <=
+    kv_stride, N >= sum of q_len).  Returns out [N, H, d_c] (and lse [N, H])."""
+    return _ragged("tv_verify_attn_ragged", q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, max_q_len,
+                   sm_scale, out, lse, return_lse, workspace, None)
+
+
+def _ragged(fn, q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, max_q_len, sm_scale, out, lse, return_lse,
+            workspace, theta):
+    for n, t in (("q_lat", q_lat), ("q_rope", q_rope), ("c_kv", c_kv), ("k_rope", k_rope), ("parent", parent),
+                 ("prefix_len", prefix_len), ("q_len", q_len)):
+        _cuda_contig(n, t)
+    _need(q_lat.dtype == torch.float32 and q_lat.dim() == 3, "q_lat must be float32 [N, H, d_c]")
+    N, H, d_c = q_lat.shape
+    _need(q_rope.dtype == torch.float32 and q_rope.dim() == 3 and q_rope.shape[:2] == (N, H),
+          "q_rope must be float32 [N, H, d_r]")
+    d_r = q_rope.shape[2]
+    _need(c_kv.dim() == 3 and c_kv.shape[2] == d_c, "c_kv must be [B, kv_stride, d_c]")
+    B, S = c_kv.shape[:2]
+    _need(k_rope.shape == (B, S, d_r) and k_rope.dtype == c_kv.dtype, "k_rope must be [B, kv_stride, d_r] like c_kv")
+    _need(parent.dtype == torch.int32 and parent.shape == (N,), "parent must be int32 [N]")
+    _need(prefix_len.dtype == torch.int32 and prefix_len.shape == (B,), "prefix_len must be int32 [B]")
+    _need(q_len.dtype == torch.int32 and q_len.shape == (B,), "q_len must be int32 [B]")
+    dt = _kv_dtype(c_kv)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_c + d_r)
+    ws_bytes = load().tv_verify_attn_ragged_workspace_size(B, H, max_q_len, S, d_c, d_r, dt)
+    _need(ws_bytes > 0, "unsupported shape for the ragged attention")
+    if out is None:
+        out = torch.empty_like(q_lat)
+    if lse is None and return_lse:
+        lse = torch.empty(N, H, dtype=torch.float32, device=q_lat.device)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q_lat.device)
+    ws_n = workspace.numel() * workspace.element_size()
+    head = (_ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), _ptr(prefix_len), _ptr(q_len), B, H,
+            max_q_len, S, d_c, d_r, dt)
+    tail = (float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_n, _stream())
+    args = head + tail if theta is None else head + (float(theta),) + tail
+    _check(fn, getattr(load(), fn)(*args))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def verify_step_ragged(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, max_q_len: int,
+                       theta: float = 10000.0, sm_scale: float | None = None, out=None, lse=None,
+                       return_lse: bool = False, workspace=None):
+    """The whole step for a ragged batch: rotate each request's q_rope rows and
+    tree key rows in place at prefix_len[b] + depth, then the ragged attention
+    (arguments as for verify_attn_ragged)."""
+    return _ragged("tv_verify_step_ragged", q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, max_q_len,
+                   sm_scale, out, lse, return_lse, workspace, theta)
 
 
 def tree_rope(q_rope, k_rope, parent, prefix_len: int, theta: float = 10000.0):
