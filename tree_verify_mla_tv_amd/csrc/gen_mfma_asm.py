@@ -25,23 +25,26 @@ TV_STEP_ASM -- per wave, for tile t (scores) and tile t-1 (values):
      8..15 of the half); P(rb, h), tile t-1's bf16 weights, with ds_read_b128
      at %[pb] + 1024 (2 rb + h).
      Woven in, for tile t (all VALU, lane = one query row, 16 of its scores):
-       mask   (only when %[nm] != 0): score i becomes -inf unless bit i of
-              %[mask] is set;
+       mask   (only when %[nm] != 0, out of line behind a branch): score i
+              becomes -inf unless bit i of %[mask] is set;
        max    over the 16 scores and the other half of the wave (the lane
               l ^ 32 holds the same row: v_permlane32_swap);
        state  %[mseen] = max(%[mseen], max); %[mref] takes the max if it was
               -inf (first visible tile); %[exc] = max(%[exc], max - %[mref]);
               the reference used is max(%[mref], -FLT_MAX) (equal to %[mref]
               unless every score so far is -inf, when exp2(-inf - ref) = 0);
-       weights  s <- exp2(s - ref), packed to bf16 pairs in v[240:247], summed
-              into %[l] with bf16 dot products against (1, 1) (two partial
-              chains), and stored with ds_write_b128 at %[pw] (keys 0..15)
-              and %[pw] + 1024.
-     These ops form a dependency graph that is list-scheduled into the gaps
-     between value ops, at most VALU_PER_GAP per gap, never in the same gap
-     as an op whose result they read: with one wave per SIMD, issue is in
-     order, and a dependent op right behind its producer would hold back the
-     next matrix op.
+       weights  s <- exp2(s - ref), packed to bf16 pairs in v[240:247] and
+              stored with ds_write_b128 at %[pw] (keys 0..15) and %[pw] + 1024;
+              the row sum %[l] adds the packed (rounded) weights, unpacked
+              with a shift and a mask, in two fp32 chains.
+     These ops form a dependency graph (derived from their register
+     operands) that is list-scheduled into the gaps between value ops: at
+     most GAP_BUDGET instructions per gap counting the LDS loads and waits
+     there (one wave per SIMD issues about one instruction per 4 cycles; a
+     matrix op lasts 32), TRANS_PER_GAP transcendentals, and never in the
+     same gap as an op whose result they read.  The first read of S comes
+     S_HAZARD wait states after the last score op, right behind the mask
+     branch; ops that touch VCC or the mask's temporaries also follow it.
 All LDS fragments go through a pool of register quads v[192:239] assigned here
 (an MFMA operand must be one register quad, and an asm operand cannot be
 split); a quad is reused one matrix op after its last reader.  Waits are
@@ -55,7 +58,7 @@ TV_STAGE_ASM -- the copy alone: wave w's nine buffer_load_dwordx4 ... lds of a
   %[t] holds each row's buffer offset.
 
 Hazards handled inside the blocks: LDS data waits; the matrix-core result S
-before the first VALU read (>= 19 wait states); the M0 and offset writes a
+before the first VALU read (>= S_HAZARD wait states); the M0 and offset writes a
 matrix op before the DMA load that reads them; v_permlane32_swap two wait
 states after the VALU write of its operand; every transcendental result used
 a matrix op or more later; the accumulators before anything outside the
