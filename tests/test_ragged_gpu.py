@@ -146,3 +146,13 @@ def test_ragged_step(dt):
         e = errors(out[s:s + q], ref["out"][0])
         assert e["max_rel"] <= TOL[dt]["max_rel"], (b, e)
         s += q
+
+
+def test_ragged_many_row_blocks_tail_pieces():
+    """Enough row blocks to fill the GPU: full row blocks stay whole and each
+    request's partial last block is cut into pieces on the device."""
+    rng = np.random.default_rng(12)
+    B = 20
+    q_lens = [int(x) for x in rng.integers(17, 65, size=B)]
+    prefixes = [int(x) for x in rng.integers(100, 3000, size=B)]
+    _check(q_lens, prefixes, 64, 512, 64, "bf16")

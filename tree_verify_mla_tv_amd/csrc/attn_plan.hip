@@ -15,6 +15,7 @@ namespace tv {
 namespace {
 constexpr int kNumCU = 256;          // MI355X; fixed so plans depend on shapes only
 constexpr int kMinKeysPerSplit = 256;
+constexpr int kMinKeysPerTailPiece = 1024;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -109,12 +110,14 @@ AttnPlan plan_attention(const AttnShape& s) {
   return p;
 }
 
-// Ragged batch: the same choice of kernel and split count, made from upper
-// bounds (B requests of at most max_q_len nodes over at most kv_stride keys);
-// each request then cuts its own kv range into pieces of the same size, so
-// shorter requests get fewer pieces.  units, n_slots and merge_blocks are
-// upper bounds (the launch sizes); the workspace starts with the request
-// records.
+// Ragged batch: the same choices as plan_attention, made from upper bounds (B
+// requests of at most max_q_len nodes over at most kv_stride keys).  With too
+// few row blocks to fill the GPU, every row block's kv range is cut into
+// pieces of chunk_full keys (shorter requests get fewer pieces).  Otherwise
+// full row blocks stay whole and the prep kernel cuts each request's partial
+// last row block into as many pieces (at most kMaxTailSplit) as fill the last
+// round of workgroups.  units, n_slots and merge_blocks are upper bounds (the
+// launch sizes); the workspace starts with the request records.
 AttnPlan plan_attention_ragged(const AttnShape& s) {
   AttnPlan p{};
   const bool mfma = s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
@@ -123,18 +126,25 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
   p.keys_per_tile = mfma ? kMfmaKeys : kValuKeys;
   p.n_rb = ceil_div(static_cast<long long>(s.q_len) * s.H, p.rows_per_block);
   p.full_rb = p.n_rb;
-  const long long target = mfma ? kNumCU : 2 * kNumCU;
+  p.target = mfma ? kNumCU : 2 * kNumCU;
   const long long blocks = static_cast<long long>(s.B) * p.n_rb;
-  if (blocks < target)
-    cut_for_blocks(s.kv_len, blocks, target, p.keys_per_tile, 10, p.split_full, p.chunk_full);
-  else
-    cut(s.kv_len, 1, p.keys_per_tile, p.split_full, p.chunk_full);
+  if (blocks < p.target) {
+    cut_for_blocks(s.kv_len, blocks, p.target, p.keys_per_tile, 10, p.split_full, p.chunk_full);
+    p.tail_pieces = false;
+    p.units = blocks * p.split_full;
+    p.n_slots = p.split_full > 1 ? p.units : 0;
+    p.merge_blocks = p.split_full > 1 ? blocks : 0;
+  } else {
+    p.split_full = 1;
+    p.chunk_full = ceil_div(s.kv_len, p.keys_per_tile) * p.keys_per_tile;
+    p.tail_pieces = true;
+    p.units = static_cast<long long>(s.B) * (p.n_rb + kMaxTailSplit);
+    p.n_slots = static_cast<long long>(s.B) * kMaxTailSplit;
+    p.merge_blocks = s.B;
+  }
   p.split_tail = p.split_full;
   p.chunk_tail = p.chunk_full;
-  p.units = blocks * p.split_full;
-  p.n_slots = p.split_full > 1 ? p.units : 0;
-  p.merge_blocks = p.split_full > 1 ? blocks : 0;
-  const size_t rec = align256((static_cast<size_t>(s.B) * kReqFields + 2) * sizeof(int32_t));
+  const size_t rec = align256((static_cast<size_t>(s.B) * kReqFields + kReqTotals) * sizeof(int32_t));
   p.ws_bytes = rec;
   p.ws_o_off = p.ws_m_off = p.ws_l_off = rec;
   if (p.n_slots > 0) {
@@ -148,70 +158,132 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
 
 namespace {
 
-// Request records of a ragged batch (one workgroup of 1024 threads): lengths
-// clamped into the bounds (q_len to [0, max_q], prefix to [0, kv_stride -
-// q_len]), row blocks, kv pieces, and the first unit, slot and merged block of
-// each request (exclusive scans over the batch), then the totals.
+static_assert(kMfmaKeys == kValuKeys, "piece sizes of the partial blocks are whole tiles of either kernel");
+
+// Request records of a ragged batch (one workgroup of 1024 threads).  Lengths
+// are clamped into the bounds (q_len to [0, max_q], prefix to [0, kv_stride -
+// q_len]).  Per request: full row blocks and their pieces, the pieces of the
+// partial last block, and (exclusive scans over the batch) its first node,
+// full-block unit, partial-block unit, slot and merged block; then the totals.
+struct ReqShape {
+  int q, P, n_full, split, tsplit, tchunk;
+};
+
+__device__ __forceinline__ ReqShape req_shape(const int32_t* prefix_len, const int32_t* q_len, int b, int H, int max_q,
+                                              int kv_stride, int rpb, int chunk, bool tail_pieces, int g_tsplit) {
+  ReqShape r;
+  r.q = min(max(q_len[b], 0), max_q);
+  r.P = min(max(prefix_len[b], 0), kv_stride - r.q);
+  const int R = r.q * H;
+  const int kv = r.P + r.q;
+  r.n_full = R / rpb;
+  r.split = tail_pieces ? 1 : max((kv + chunk - 1) / chunk, 1);
+  r.tsplit = 0;
+  r.tchunk = 0;
+  if (R % rpb != 0) {
+    if (!tail_pieces) {
+      r.tsplit = r.split;
+      r.tchunk = chunk;
+    } else {
+      // Pieces of at least kMinKeysPerTailPiece keys: a unit's set-up (~10
+      // tile-steps) should stay small next to its sweep.
+      const int want = min(g_tsplit, max(1, kv / kMinKeysPerTailPiece));
+      r.tchunk = (((kv + want - 1) / want + kMfmaKeys - 1) / kMfmaKeys) * kMfmaKeys;  // whole tiles (both kernels: 32 keys)
+      r.tsplit = (kv + r.tchunk - 1) / r.tchunk;
+    }
+  }
+  return r;
+}
+
 __global__ __launch_bounds__(1024) void ragged_prep_kernel(const int32_t* __restrict__ prefix_len,
                                                            const int32_t* __restrict__ q_len, int B, int H,
                                                            int max_q, int kv_stride, int rpb, int chunk,
-                                                           int32_t* __restrict__ rq) {
-  __shared__ int s_scan[4][1024];
+                                                           int tail_pieces, int target, int32_t* __restrict__ rq) {
+  constexpr int kN = 5;  // nodes, full-block units, partial-block units, slots, merged blocks
+  __shared__ int s_scan[kN][1024];
+  __shared__ int s_tsplit;
   const int t = threadIdx.x;
   const int per = (B + 1023) / 1024;
   const int b0 = min(B, t * per);
   const int b1 = min(B, b0 + per);
-  // Per request: nodes, units, slots, merged blocks.
-  auto shape = [&](int b, int& q, int& P, int& n_rb, int& n_split) {
-    q = min(max(q_len[b], 0), max_q);
-    P = min(max(prefix_len[b], 0), kv_stride - q);
-    n_rb = (q * H + rpb - 1) / rpb;
-    n_split = max((P + q + chunk - 1) / chunk, 1);
-  };
-  int sum[4] = {0, 0, 0, 0};
+  // Pieces of the partial blocks: fill what the full blocks leave of their
+  // last round (a round more if that is less than one piece per block).
+  int g_tsplit = 1;
+  if (tail_pieces) {
+    int full = 0, part = 0;
+    for (int b = b0; b < b1; ++b) {
+      const ReqShape r = req_shape(prefix_len, q_len, b, H, max_q, kv_stride, rpb, chunk, false, 1);
+      full += r.n_full;
+      part += r.tsplit > 0;
+    }
+    s_scan[0][t] = full;
+    s_scan[1][t] = part;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+      if (t < off) {
+        s_scan[0][t] += s_scan[0][t + off];
+        s_scan[1][t] += s_scan[1][t + off];
+      }
+      __syncthreads();
+    }
+    if (t == 0) {
+      const int n_part = s_scan[1][0];
+      int free_slots = target - s_scan[0][0] % target;
+      if (free_slots < n_part) free_slots += target;
+      s_tsplit = min(max(free_slots / max(n_part, 1), 1), kMaxTailSplit);
+    }
+    __syncthreads();
+    g_tsplit = s_tsplit;
+    __syncthreads();
+  }
+  int sum[kN] = {0, 0, 0, 0, 0};
   for (int b = b0; b < b1; ++b) {
-    int q, P, n_rb, n_split;
-    shape(b, q, P, n_rb, n_split);
-    sum[0] += q;
-    sum[1] += n_rb * n_split;
-    sum[2] += n_split > 1 ? n_rb * n_split : 0;
-    sum[3] += n_split > 1 ? n_rb : 0;
+    const ReqShape r = req_shape(prefix_len, q_len, b, H, max_q, kv_stride, rpb, chunk, tail_pieces, g_tsplit);
+    sum[0] += r.q;
+    sum[1] += r.n_full * r.split;
+    sum[2] += r.tsplit;
+    sum[3] += (r.split > 1 ? r.n_full * r.split : 0) + (r.tsplit > 1 ? r.tsplit : 0);
+    sum[4] += (r.split > 1 ? r.n_full : 0) + (r.tsplit > 1 ? 1 : 0);
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) s_scan[k][t] = sum[k];
+  for (int k = 0; k < kN; ++k) s_scan[k][t] = sum[k];
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    int v[4];
+    int v[kN];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = t >= off ? s_scan[k][t - off] : 0;
+    for (int k = 0; k < kN; ++k) v[k] = t >= off ? s_scan[k][t - off] : 0;
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) s_scan[k][t] += v[k];
+    for (int k = 0; k < kN; ++k) s_scan[k][t] += v[k];
     __syncthreads();
   }
-  int run[4];
+  int run[kN];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) run[k] = s_scan[k][t] - sum[k];
+  for (int k = 0; k < kN; ++k) run[k] = s_scan[k][t] - sum[k];
   for (int b = b0; b < b1; ++b) {
-    int q, P, n_rb, n_split;
-    shape(b, q, P, n_rb, n_split);
-    int32_t* r = rq + b * kReqFields;
-    r[kReqQStart] = run[0];
-    r[kReqQLen] = q;
-    r[kReqPrefix] = P;
-    r[kReqNRb] = n_rb;
-    r[kReqSplit] = n_split;
-    r[kReqUnit0] = run[1];
-    r[kReqSlot0] = run[2];
-    r[kReqMerge0] = run[3];
-    run[0] += q;
-    run[1] += n_rb * n_split;
-    run[2] += n_split > 1 ? n_rb * n_split : 0;
-    run[3] += n_split > 1 ? n_rb : 0;
+    const ReqShape r = req_shape(prefix_len, q_len, b, H, max_q, kv_stride, rpb, chunk, tail_pieces, g_tsplit);
+    int32_t* o = rq + b * kReqFields;
+    o[kReqQStart] = run[0];
+    o[kReqQLen] = r.q;
+    o[kReqPrefix] = r.P;
+    o[kReqNFull] = r.n_full;
+    o[kReqSplit] = r.split;
+    o[kReqTSplit] = r.tsplit;
+    o[kReqTChunk] = r.tchunk;
+    o[kReqFull0] = run[1];
+    o[kReqTail0] = run[2];
+    o[kReqSlot0] = run[3];
+    o[kReqMerge0] = run[4];
+    run[0] += r.q;
+    run[1] += r.n_full * r.split;
+    run[2] += r.tsplit;
+    run[3] += (r.split > 1 ? r.n_full * r.split : 0) + (r.tsplit > 1 ? r.tsplit : 0);
+    run[4] += (r.split > 1 ? r.n_full : 0) + (r.tsplit > 1 ? 1 : 0);
   }
   if (t == 1023) {
     rq[B * kReqFields] = s_scan[1][1023];
-    rq[B * kReqFields + 1] = s_scan[3][1023];
+    rq[B * kReqFields + 1] = s_scan[1][1023] + s_scan[2][1023];
+    rq[B * kReqFields + 2] = s_scan[4][1023];
   }
 }
 
@@ -234,12 +306,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, lo
   int rb, n_split, R;
   long long slot0, row0;
   if (a.req) {
-    if (mb >= a.req[a.B * kReqFields + 1]) return;
+    if (mb >= a.req[a.B * kReqFields + 2]) return;
     const int bq = find_request(a.req, a.B, kReqMerge0, mb);
     const int32_t* rec = a.req + bq * kReqFields;
-    rb = static_cast<int>(mb - rec[kReqMerge0]);
-    n_split = rec[kReqSplit];
-    slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(rb) * n_split;
+    const int m = static_cast<int>(mb - rec[kReqMerge0]);
+    const int split = rec[kReqSplit];
+    const int full_merges = split > 1 ? rec[kReqNFull] : 0;
+    if (m < full_merges) {  // a full row block
+      rb = m;
+      n_split = split;
+      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(m) * split;
+    } else {  // the partial last row block
+      rb = rec[kReqNFull];
+      n_split = rec[kReqTSplit];
+      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(full_merges) * split;
+    }
     R = rec[kReqQLen] * a.H;
     row0 = static_cast<long long>(rec[kReqQStart]) * a.H;
   } else if (mb < full_blocks) {
@@ -295,7 +376,8 @@ hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const Attn
 hipError_t launch_ragged_prep(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, const int32_t* prefix_len,
                               const int32_t* q_len, hipStream_t stream) {
   ragged_prep_kernel<<<dim3(1), 1024, 0, stream>>>(prefix_len, q_len, s.B, s.H, s.q_len, s.kv_len,
-                                                   plan.rows_per_block, plan.chunk_full, const_cast<int32_t*>(a.req));
+                                                   plan.rows_per_block, plan.chunk_full, plan.tail_pieces ? 1 : 0,
+                                                   static_cast<int>(plan.target), const_cast<int32_t*>(a.req));
   return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ struct AttnPlan {
   int split_full, chunk_full;
   int split_tail, chunk_tail;  // meaningful when full_rb < n_rb
   long long units;
+  long long target;            // workgroups that run at once (ragged plans)
+  bool tail_pieces;            // ragged: cut the partial last row blocks into pieces on the device
   long long n_slots;           // partial-result slots in the workspace
   long long merge_blocks;      // row blocks that need merging
   size_t ws_bytes;
@@ -105,19 +107,28 @@ struct AttnArgs {
   int chunk;      // keys per kv piece
 };
 
-// Request record of a ragged batch: [B][kReqFields] int32, then the totals
-// (units, merge blocks).
+// Request record of a ragged batch: [B][kReqFields] int32, then kReqTotals
+// totals (units of full row blocks, all units, merged blocks).  Units of full
+// row blocks come first in launch order, request by request; the pieces of
+// the partial last row blocks after them.
 enum ReqField : int {
   kReqQStart = 0,  // first node of the request in the packed node arrays
   kReqQLen,        // nodes (0 .. max_q_len)
   kReqPrefix,      // prefix rows
-  kReqNRb,         // row blocks
-  kReqSplit,       // kv pieces per row block
-  kReqUnit0,       // first unit
-  kReqSlot0,       // first partial-result slot (when split > 1)
-  kReqMerge0,      // first merged row block (when split > 1)
+  kReqNFull,       // full row blocks
+  kReqSplit,       // kv pieces per full row block
+  kReqTSplit,      // kv pieces of the partial last row block (0: no such block)
+  kReqTChunk,      // keys per piece of the partial block
+  kReqFull0,       // first unit of the full blocks
+  kReqTail0,       // first unit of the partial block, counted from the end of all full-block units
+  kReqSlot0,       // first partial-result slot
+  kReqMerge0,      // first merged row block
   kReqFields
 };
+constexpr int kReqTotals = 3;
+// Most pieces the partial last row block of a request is cut into (to fill
+// the last round of workgroups).
+constexpr int kMaxTailSplit = 16;
 
 // The work of one unit (one workgroup), with the shape of its request.
 struct Unit {
@@ -164,52 +175,6 @@ __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long long u) {
   return w;
 }
 
-// Last request whose first entry in column `field` is <= v (requests with
-// nothing to do share that entry with the next one, so the search lands on the
-// request that owns v).
-__device__ __forceinline__ int find_request(const int32_t* rq, int B, int field, long long v) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (rq[mid * kReqFields + field] <= v) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Ragged batch: block x of the launch (an upper bound of units) -> its unit,
-// or false past the batch's real total.  Units are numbered request by
-// request, then kv range, then row block; the first multiple of 8 of the
-// real total is dealt XCD by XCD as for a uniform batch.
-__device__ __forceinline__ bool decode_unit_ragged(const AttnArgs& a, long long x, Unit& w) {
-  const int32_t* rq = a.req;
-  const long long total = rq[a.B * kReqFields];
-  if (x >= total) return false;
-  constexpr int kXcds = 8;
-  const long long f8 = total / kXcds * kXcds;
-  const long long u = x < f8 ? (x % kXcds) * (f8 / kXcds) + x / kXcds : x;
-  const int b = find_request(rq, a.B, kReqUnit0, u);
-  const int32_t* r = rq + b * kReqFields;
-  const int local = static_cast<int>(u - r[kReqUnit0]);
-  const int n_rb = r[kReqNRb];
-  const int n_split = r[kReqSplit];
-  w.b = b;
-  w.rb = local % n_rb;
-  w.split = local / n_rb;
-  w.q_len = r[kReqQLen];
-  w.P = r[kReqPrefix];
-  w.R = w.q_len * a.H;
-  w.kv_len = w.P + w.q_len;
-  w.k_begin = w.split * a.chunk;
-  w.k_end = min(w.kv_len, w.k_begin + a.chunk);
-  w.slot = n_split > 1 ? static_cast<long long>(r[kReqSlot0]) + static_cast<long long>(w.rb) * n_split + w.split
-                       : -1;
-  w.row0 = static_cast<long long>(r[kReqQStart]) * a.H;
-  w.par0 = r[kReqQStart];
-  w.kv_row0 = static_cast<long long>(b) * a.kv_stride;
-  return true;
-}
-
 // Workgroup x of a launch runs on XCD x % 8 (the hardware deals workgroups to
 // the 8 XCDs in turn), and each XCD has its own L2.  Units are numbered tree by
 // tree, full row blocks first, then the pieces of the split tail blocks; this
@@ -227,6 +192,74 @@ __device__ __forceinline__ long long unit_of_block(const AttnArgs& a, long long 
   const long long r8 = (units - f8) / kXcds * kXcds;
   if (p < r8) return f8 + (p % kXcds) * (r8 / kXcds) + p / kXcds;
   return x;
+}
+
+// Last request whose first entry in column `field` is <= v (requests with
+// nothing to do share that entry with the next one, so the search lands on the
+// request that owns v).
+__device__ __forceinline__ int find_request(const int32_t* rq, int B, int field, long long v) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rq[mid * kReqFields + field] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Ragged batch: block x of the launch (an upper bound of units) -> its unit,
+// or false past the batch's real total.  The real units are dealt to the XCDs
+// as unit_of_block deals a uniform batch's (full-block units, then pieces).
+__device__ __forceinline__ bool decode_unit_ragged(const AttnArgs& a, long long x, Unit& w) {
+  const int32_t* rq = a.req;
+  const long long u_full = rq[a.B * kReqFields];
+  const long long total = rq[a.B * kReqFields + 1];
+  if (x >= total) return false;
+  constexpr int kXcds = 8;
+  const long long f8 = u_full / kXcds * kXcds;
+  long long u = x;
+  if (x < f8) {
+    u = (x % kXcds) * (f8 / kXcds) + x / kXcds;
+  } else {
+    const long long p = x - f8;
+    const long long r8 = (total - f8) / kXcds * kXcds;
+    if (p < r8) u = f8 + (p % kXcds) * (r8 / kXcds) + p / kXcds;
+  }
+  int b, chunk;
+  const int32_t* r;
+  if (u < u_full) {
+    b = find_request(rq, a.B, kReqFull0, u);
+    r = rq + b * kReqFields;
+    const int local = static_cast<int>(u - r[kReqFull0]);
+    const int n_full = r[kReqNFull];
+    const int n_split = r[kReqSplit];
+    w.rb = local % n_full;
+    w.split = local / n_full;
+    chunk = a.chunk;
+    w.slot = n_split > 1 ? static_cast<long long>(r[kReqSlot0]) + static_cast<long long>(w.rb) * n_split + w.split
+                         : -1;
+  } else {
+    b = find_request(rq, a.B, kReqTail0, u - u_full);
+    r = rq + b * kReqFields;
+    const int piece = static_cast<int>(u - u_full - r[kReqTail0]);
+    const int n_split = r[kReqSplit];
+    const long long full_slots = n_split > 1 ? static_cast<long long>(r[kReqNFull]) * n_split : 0;
+    w.rb = r[kReqNFull];
+    w.split = piece;
+    chunk = r[kReqTChunk];
+    w.slot = r[kReqTSplit] > 1 ? r[kReqSlot0] + full_slots + piece : -1;
+  }
+  w.b = b;
+  w.q_len = r[kReqQLen];
+  w.P = r[kReqPrefix];
+  w.R = w.q_len * a.H;
+  w.kv_len = w.P + w.q_len;
+  w.k_begin = w.split * chunk;
+  w.k_end = min(w.kv_len, w.k_begin + chunk);
+  w.row0 = static_cast<long long>(r[kReqQStart]) * a.H;
+  w.par0 = r[kReqQStart];
+  w.kv_row0 = static_cast<long long>(b) * a.kv_stride;
+  return true;
 }
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
