@@ -183,6 +183,65 @@ def next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, with_oracle: bool) -> 
     return out
 
 
+def verify_variants(torch, tv, W) -> dict:
+    """The verify attention beyond the serving batch: a long prefix with one
+    request, a ragged batch of mixed prefixes and tree sizes, and a 256-node
+    tree.  Synthetic bf16 caches (N(0,1) x 0.5), branching trees; flops counted
+    on the visible (row, key) pairs."""
+    import numpy as np
+    dev = "cuda:0"
+    H, d_c, d_r = 64, 512, 64
+    sm = 1.0 / (d_c + d_r) ** 0.5
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    rng = np.random.default_rng(7)
+
+    def visible_pairs(parent_rows, P):
+        depth = np.zeros(len(parent_rows), dtype=np.int64)
+        for i in range(1, len(parent_rows)):
+            depth[i] = depth[parent_rows[i]] + 1
+        return int((P + depth + 1).sum())
+
+    def cache(B, S):
+        return ((torch.randn(B, S, d_c, device=dev, generator=g) * 0.5).to(torch.bfloat16),
+                (torch.randn(B, S, d_r, device=dev, generator=g) * 0.5).to(torch.bfloat16))
+
+    out = {}
+    # One request, 200k-token prefix (kv split into pieces + merge).
+    for name, B, q, P in (("long_prefix_b1_p200000_q33", 1, 33, 200000), ("big_tree_b4_p4096_q256", 4, 256, 4096)):
+        q_lat = torch.randn(B, q, H, d_c, device=dev, generator=g) * 0.5
+        q_rope = torch.randn(B, q, H, d_r, device=dev, generator=g) * 0.5
+        c_kv, k_rope = cache(B, P + q)
+        par = np.stack([W.tree_branch(q, rng) for _ in range(B)]).astype(np.int32)
+        parent = torch.from_numpy(par).to(dev)
+        o = torch.empty_like(q_lat)
+        ws = torch.empty(max(tv.workspace_size(B, H, q, P, d_c, d_r, tv.TV_BF16), 1), dtype=torch.uint8, device=dev)
+        ms = _time_ms(torch, lambda: tv.verify_attn(q_lat, q_rope, c_kv, k_rope, parent, P, sm, out=o, workspace=ws),
+                      10)
+        flops = H * sum(visible_pairs(par[b], P) for b in range(B)) * (2 * (d_c + d_r) + 2 * d_c)
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        del q_lat, q_rope, c_kv, k_rope, o, ws
+    # Ragged: 32 requests, q_len in {9, 17, 33}, prefixes 2k-16k.
+    q_lens = [int(x) for x in rng.choice([9, 17, 33], 32)]
+    prefixes = [int(x) for x in rng.integers(2048, 16384, 32)]
+    B, N, S = 32, sum(q_lens), max(p + q for p, q in zip(prefixes, q_lens))
+    q_lat = torch.randn(N, H, d_c, device=dev, generator=g) * 0.5
+    q_rope = torch.randn(N, H, d_r, device=dev, generator=g) * 0.5
+    c_kv, k_rope = cache(B, S)
+    pars = [W.tree_branch(q, rng).astype(np.int32) for q in q_lens]
+    parent = torch.from_numpy(np.concatenate(pars)).to(dev)
+    pl = torch.tensor(prefixes, dtype=torch.int32, device=dev)
+    ql = torch.tensor(q_lens, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q_lat)
+    ws = torch.empty(tv.load().tv_verify_attn_ragged_workspace_size(B, H, max(q_lens), S, d_c, d_r, tv.TV_BF16),
+                     dtype=torch.uint8, device=dev)
+    ms = _time_ms(torch, lambda: tv.verify_attn_ragged(q_lat, q_rope, c_kv, k_rope, parent, pl, ql, max(q_lens), sm,
+                                                       out=o, workspace=ws), 10)
+    flops = H * sum(visible_pairs(p_, P) for p_, P in zip(pars, prefixes)) * (2 * (d_c + d_r) + 2 * d_c)
+    out["ragged_b32_q9to33_p2kto16k"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +361,7 @@ def main() -> int:
         rec["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_sample, w.B))
     if args.next_rows and w.kv_dtype == "bf16":
         rec["next_rows"] = next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, args.cpu_sample > 0)
+        rec["next_rows"]["verify_variants"] = verify_variants(torch, tv, W)
     print(json.dumps(rec), flush=True)
     return 0
 
