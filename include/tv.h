@@ -57,9 +57,10 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype_t;
  * words per node. */
 #define TV_MAX_Q_LEN 256
 
-/* Largest draft budget of tv_tree_build (one frontier entry per lane of a
- * 64-wide wave). */
-#define TV_MAX_BUILD_BUDGET 63
+/* Largest draft budget of tv_tree_build (a tree of TV_MAX_Q_LEN nodes with
+ * its root), and the most ranked candidates it holds: min(D, budget) * K. */
+#define TV_MAX_BUILD_BUDGET (TV_MAX_Q_LEN - 1)
+#define TV_MAX_BUILD_CANDIDATES 8192
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* tv_status_str(tv_status_t s);
@@ -291,7 +292,8 @@ tv_status_t tv_kv_compact(void* c_kv, void* k_rope, tv_dtype_t kv_dtype, const i
  *   root), score f32 (0 for the root); slots past the drafted nodes hold -1, -1,
  *   -1, -inf.  n_nodes int32 [B]: drafted nodes (budget unless the candidates
  *   run out: K + K^2 + ... + K^D < budget).
- *   1 <= K <= 64, D >= 1, 0 <= budget <= TV_MAX_BUILD_BUDGET, B >= 1.
+ *   1 <= K <= 64, D >= 1, 0 <= budget <= TV_MAX_BUILD_BUDGET, B >= 1,
+ *   min(D, budget) * K <= TV_MAX_BUILD_CANDIDATES (else TV_ERR_UNSUPPORTED).
  */
 tv_status_t tv_tree_build(const float* logp, const int32_t* cand_tok, const int32_t* root_tok, int32_t B, int32_t D,
                           int32_t K, int32_t budget, int32_t* parent, int32_t* token, int32_t* depth, float* score,

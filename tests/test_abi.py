@@ -173,7 +173,9 @@ def test_tree_build_rejects_before_launch():
     assert f(*args(D=0)) == INV
     assert f(*args(B=0)) == INV
     assert f(*args(budget=-1)) == INV
-    assert f(*args(budget=64)) == UNS
+    assert f(*args(budget=256)) == UNS
+    assert f(*args(D=200, K=64, budget=200)) == UNS   # 12800 ranked candidates
+    assert f(*args(D=128, K=65, budget=200)) == UNS
     assert f(*args(lp=None)) == INV
     assert f(*args(lp=A + 2)) == INV
     assert f(*args(out=None)) == INV

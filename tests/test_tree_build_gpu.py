@@ -53,6 +53,11 @@ def test_serving_shape(seed):
     (3, 8, 4, 0, True, 0.5),        # no draft nodes
     (3, 8, 4, 1, False, 0.5),
     (1000, 12, 6, 40, False, 0.3),  # many requests
+    (3, 300, 4, 255, False, 0.3),   # largest budget: four frontier slots per lane
+    (2, 128, 64, 255, False, 1.0),  # most ranked candidates (128 depths x 64)
+    (4, 255, 1, 255, True, 0.5),    # a 255-node chain
+    (3, 1, 64, 255, False, 0.5),    # a star that runs out at 64
+    (5, 40, 3, 100, True, 0.2),
 ])
 def test_shapes(B, D, K, budget, sort, alpha):
     x = W.make_build_inputs(B, D, K, seed=B * 7 + D + K, sort=sort, alpha=alpha)
@@ -66,6 +71,17 @@ def test_all_tied(value):
     tok = np.arange(B * D * K, dtype=np.int32).reshape(B, D, K)
     par, n = _check(lp, tok, np.array([1, 2, 3]), 63)
     assert list(par[0, 1:8]) == [0, 0, 0, 1, 1, 1, 2]  # breadth-first
+
+
+def test_all_tied_largest_budget():
+    """255 draft nodes, every log-prob equal: the breadth-first numbering of
+    the complete ternary tree, across all four frontier slots of each lane."""
+    B, D, K = 2, 12, 3
+    lp = np.zeros((B, D, K), dtype=np.float32)
+    tok = np.arange(B * D * K, dtype=np.int32).reshape(B, D, K)
+    par, n = _check(lp, tok, np.array([5, 6]), 255)
+    assert (n == 255).all()
+    assert all(par[0, i] == (i - 1) // K for i in range(1, 256))
 
 
 def test_nan_inf_and_integer_ties():

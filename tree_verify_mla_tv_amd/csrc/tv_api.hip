@@ -342,6 +342,7 @@ tv_status_t tv_tree_build(const float* logp, const int32_t* cand_tok, const int3
                           int32_t* n_nodes, hipStream_t stream) {
   if (B < 1 || D < 1 || K < 1 || budget < 0) return TV_ERR_INVALID;
   if (K > 64 || budget > TV_MAX_BUILD_BUDGET) return TV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(D < budget ? D : budget) * K > TV_MAX_BUILD_CANDIDATES) return TV_ERR_UNSUPPORTED;
   const void* ptrs[] = {logp, cand_tok, root_tok, parent, token, depth, score, n_nodes};
   for (const void* p : ptrs)
     if (!p || (reinterpret_cast<uintptr_t>(p) & 3u)) return TV_ERR_INVALID;

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libtv.so")
 TV_OK, TV_ERR_INVALID, TV_ERR_UNSUPPORTED, TV_ERR_LAUNCH = 0, 1, 2, 3
 TV_F32, TV_BF16 = 0, 1
 TV_MAX_Q_LEN = 256
-TV_MAX_BUILD_BUDGET = 63
+TV_MAX_BUILD_BUDGET = TV_MAX_Q_LEN - 1
+TV_MAX_BUILD_CANDIDATES = 8192
 
 _lib = None
 
