@@ -183,6 +183,25 @@ def next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, with_oracle: bool) -> 
     return out
 
 
+def reference_gemm(torch, n: int = 8192, reps: int = 10) -> dict:
+    """The vendor bf16 GEMM (torch.matmul, hipBLASLt) on N(0,1) operands, timed
+    on the same box: what dense bf16 matrix work reaches here with random data
+    (the part runs at its power limit, so this sits well below the datasheet
+    peak).  Context for roofline.frac, not a competitor."""
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(3)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    ms = _time_ms(torch, lambda: torch.matmul(a, b, out=c), reps)
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) operands", "tflops": round(tf, 1),
+            "frac_of_peak": round(tf / PEAKS_TFLOPS["bf16"], 4)}
+
+
 def verify_variants(torch, tv, W) -> dict:
     """The verify attention beyond the serving batch: a long prefix with one
     request, a ragged batch of mixed prefixes and tree sizes, and a 256-node
@@ -357,6 +376,8 @@ def main() -> int:
             "achieved_hbm_gbs": round(counts["attn_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
         },
     }
+    if w.kv_dtype == "bf16":
+        rec["roofline"]["reference_gemm"] = reference_gemm(torch)
     if args.cpu_sample > 0:
         rec["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_sample, w.B))
     if args.next_rows and w.kv_dtype == "bf16":
