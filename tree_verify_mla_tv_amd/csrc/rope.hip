@@ -17,12 +17,16 @@ namespace tv {
 
 // The rotation itself.  Contraction into FMA is disabled so that each product
 // and each sum is rounded in float64 exactly as written.
-__device__ __forceinline__ void rotate_pair_f64(double x1, double x2, double ang, double& y1, double& y2) {
+__device__ __forceinline__ void rotate_cs_f64(double x1, double x2, double c, double s, double& y1, double& y2) {
 #pragma clang fp contract(off)
-  double s, c;
-  sincos(ang, &s, &c);
   y1 = x1 * c - x2 * s;
   y2 = x2 * c + x1 * s;
+}
+
+__device__ __forceinline__ void rotate_pair_f64(double x1, double x2, double ang, double& y1, double& y2) {
+  double s, c;
+  sincos(ang, &s, &c);
+  rotate_cs_f64(x1, x2, c, s, y1, y2);
 }
 
 template <typename T>
@@ -73,12 +77,15 @@ __global__ __launch_bounds__(64) void tree_positions_kernel(const int32_t* __res
   for (int i = threadIdx.x; i < q_len; i += blockDim.x) pos[static_cast<int64_t>(b) * q_len + i] = prefix_len + s_depth[i];
 }
 
-// The step's rotation: for tree b (blockIdx.y), every query row q_rope[b,i,h,:]
-// and the tree's own key row k_rope[b, prefix+i, :] turn at prefix + depth(i).
-// blockIdx.x strides over the (node, head-or-key, pair) triples of the tree.
-// A ragged batch (req non-null) takes each request's node range, node count
-// and prefix from its record; its query rows are packed request after request
-// and its key rows start at b * kv_len (kv_len = the cache stride).
+// The step's rotation: for tree b (blockIdx.y) and node i (blockIdx.x), the
+// node's H query rows q_rope[b,i,h,:] and the tree's own key row
+// k_rope[b, prefix+i, :] turn at prefix + depth(i).  Every row of a node shares
+// its angles, so the block evaluates the float64 cos/sin of each pair once (in
+// LDS) and rotates the H + 1 rows with them: the same values, rounded the same
+// way, as evaluating them per row.  A ragged batch (req non-null) takes each
+// request's node range, node count and prefix from its record; its query rows
+// are packed request after request and its key rows start at b * kv_len
+// (kv_len = the cache stride).
 template <typename KV>
 __global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_rope,
                                                         typename KV::storage* __restrict__ k_rope,
@@ -86,8 +93,11 @@ __global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_ro
                                                         int half, int prefix_len, int kv_len, RopeFreq f,
                                                         const int32_t* __restrict__ req) {
   __shared__ int s_parent[kMaxQ];
-  __shared__ int s_depth[kMaxQ];
+  __shared__ double s_cos[kMaxHalf];
+  __shared__ double s_sin[kMaxHalf];
+  __shared__ int s_depth;
   const int b = blockIdx.y;
+  const int i = blockIdx.x;
   int64_t node0 = static_cast<int64_t>(b) * q_len;
   if (req) {
     const int32_t* r = req + b * kReqFields;
@@ -95,24 +105,39 @@ __global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_ro
     q_len = r[kReqQLen];
     prefix_len = r[kReqPrefix];
   }
-  tree_depths_lds(parent + node0, q_len, s_parent, s_depth);
+  if (i >= q_len) return;  // the whole block
+  // Node i's ancestors all have indices below i (parents are clamped).
+  for (int j = threadIdx.x; j <= i; j += blockDim.x) s_parent[j] = clamp_parent(parent[node0 + j], j);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int d = 0;
+    for (int n = s_parent[i]; n >= 0; n = s_parent[n]) ++d;
+    s_depth = d;
+  }
+  __syncthreads();
+  const double pos = static_cast<double>(prefix_len + s_depth);
+  for (int k = threadIdx.x; k < half; k += blockDim.x) {
+    double sn, cs;
+    sincos(pos * f.inv_freq[k], &sn, &cs);
+    s_sin[k] = sn;
+    s_cos[k] = cs;
+  }
+  __syncthreads();
   const int per_node = (H + 1) * half;
-  const int total = q_len * per_node;
-  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
-    const int i = idx / per_node;
-    const int rem = idx - i * per_node;
-    const int h = rem / half;
-    const int k = rem - h * half;
-    const double ang = static_cast<double>(prefix_len + s_depth[i]) * f.inv_freq[k];
+  for (int idx = threadIdx.x; idx < per_node; idx += blockDim.x) {
+    const int h = idx / half;
+    const int k = idx - h * half;
+    const double c = s_cos[k];
+    const double sn = s_sin[k];
     double y1, y2;
     if (h < H) {
       float* row = q_rope + ((node0 + i) * H + h) * 2 * half;
-      rotate_pair_f64(static_cast<double>(row[k]), static_cast<double>(row[k + half]), ang, y1, y2);
+      rotate_cs_f64(static_cast<double>(row[k]), static_cast<double>(row[k + half]), c, sn, y1, y2);
       row[k] = static_cast<float>(y1);
       row[k + half] = static_cast<float>(y2);
     } else {
       typename KV::storage* row = k_rope + (static_cast<int64_t>(b) * kv_len + prefix_len + i) * 2 * half;
-      rotate_pair_f64(load_f64<KV>(row + k), load_f64<KV>(row + k + half), ang, y1, y2);
+      rotate_cs_f64(load_f64<KV>(row + k), load_f64<KV>(row + k + half), c, sn, y1, y2);
       store_from_f64<KV>(row + k, y1);
       store_from_f64<KV>(row + k + half, y2);
     }
@@ -148,16 +173,14 @@ hipError_t launch_tree_positions(const int32_t* parent, int B, int q_len, int pr
 hipError_t launch_tree_rope(float* q_rope, void* k_rope, bool bf16, const int32_t* parent, int B, int q_len, int H,
                             int d_r, int prefix_len, const RopeFreq& f, hipStream_t stream) {
   const int half = d_r / 2;
-  const int total = q_len * (H + 1) * half;
-  const int threads = 256;
-  const int bx = (total + threads - 1) / threads;
   const int kv_len = prefix_len + q_len;
+  const dim3 grid(static_cast<unsigned>(q_len), static_cast<unsigned>(B));
   if (bf16)
-    tree_rope_kernel<BF16><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, q_len,
-                                                                 H, half, prefix_len, kv_len, f, nullptr);
+    tree_rope_kernel<BF16><<<grid, 256, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, q_len, H, half,
+                                                     prefix_len, kv_len, f, nullptr);
   else
-    tree_rope_kernel<F32><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, q_len, H,
-                                                                half, prefix_len, kv_len, f, nullptr);
+    tree_rope_kernel<F32><<<grid, 256, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, q_len, H, half,
+                                                    prefix_len, kv_len, f, nullptr);
   return hipGetLastError();
 }
 
@@ -165,15 +188,13 @@ hipError_t launch_tree_rope_ragged(float* q_rope, void* k_rope, bool bf16, const
                                    int B, int max_q, int H, int d_r, int kv_stride, const RopeFreq& f,
                                    hipStream_t stream) {
   const int half = d_r / 2;
-  const int total = max_q * (H + 1) * half;
-  const int threads = 256;
-  const int bx = (total + threads - 1) / threads;
+  const dim3 grid(static_cast<unsigned>(max_q), static_cast<unsigned>(B));
   if (bf16)
-    tree_rope_kernel<BF16><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, max_q,
-                                                                 H, half, 0, kv_stride, f, req);
+    tree_rope_kernel<BF16><<<grid, 256, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, max_q, H, half,
+                                                     0, kv_stride, f, req);
   else
-    tree_rope_kernel<F32><<<dim3(bx, B), threads, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, max_q, H,
-                                                                half, 0, kv_stride, f, req);
+    tree_rope_kernel<F32><<<grid, 256, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, max_q, H, half, 0,
+                                                    kv_stride, f, req);
   return hipGetLastError();
 }
 
