@@ -37,9 +37,11 @@ PEAKS_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32_mfma": 157.3, "f32_valu": 15
 # and the roofline that bounds it.
 KERNELS = {
     "bf16": dict(name="attn_mfma_bf16_kernel",
-                 source=["tree_verify_mla_tv_amd/csrc/attn_mfma.hip", "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h"],
+                 source=["tree_verify_mla_tv_amd/csrc/attn_mfma.hip", "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h",
+                         "tree_verify_mla_tv_amd/csrc/tv_kernels.h"],
                  bound="mfma", peak="bf16", dtype="bf16"),
-    "f32": dict(name="attn_valu_kernel", source=["tree_verify_mla_tv_amd/csrc/attn_valu.hip"], bound="alu",
+    "f32": dict(name="attn_valu_kernel", source=["tree_verify_mla_tv_amd/csrc/attn_valu.hip",
+                                                "tree_verify_mla_tv_amd/csrc/tv_kernels.h"], bound="alu",
                 peak="f32_valu", dtype="f32"),
 }
 

@@ -340,21 +340,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, lo
   }
   const int row = rb * rpb + r;
   if (row >= R) return;
+  // The pieces' loads are issued in batches with no branch between them, so a
+  // thread waits for one memory round trip per batch rather than per piece.
+  constexpr int kBatch = 8;
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, a.ws_m[(slot0 + s) * rpb + r]);
+  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (s0 + k < n_split) M = fmaxf(M, a.ws_m[(slot0 + s0 + k) * rpb + r]);
+  }
   float W = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < n_split; ++s) {
-    const long long sr = (slot0 + s) * rpb + r;
-    const float l = a.ws_l[sr];
-    if (!(l > 0.f)) continue;
-    const float w = l * expf(a.ws_m[sr] - M);
-    const float4 v = *reinterpret_cast<const float4*>(a.ws_o + sr * d_c + col4 * 4);
-    W += w;
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+    float l[kBatch], m[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const long long sr = (slot0 + s0 + k) * rpb + r;
+      const bool in = s0 + k < n_split;
+      l[k] = in ? a.ws_l[sr] : 0.f;
+      m[k] = in ? a.ws_m[sr] : 0.f;
+      v[k] = in ? *reinterpret_cast<const float4*>(a.ws_o + sr * d_c + col4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      // a piece with no visible key (row sum 0) adds nothing
+      const float w = l[k] > 0.f ? l[k] * expf(m[k] - M) : 0.f;
+      W += w;
+      acc.x = fmaf(w, v[k].x, acc.x);
+      acc.y = fmaf(w, v[k].y, acc.y);
+      acc.z = fmaf(w, v[k].z, acc.z);
+      acc.w = fmaf(w, v[k].w, acc.w);
+    }
   }
   const float inv = 1.f / W;
   const long long grow = row0 + row;

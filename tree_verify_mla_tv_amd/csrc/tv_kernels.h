@@ -182,13 +182,32 @@ __device__ __forceinline__ Unit decode_unit(const AttnArgs& a, long long u) {
 // contiguous run of pieces, so the workgroups sharing a tree's latent rows
 // mostly share one L2.  It is a bijection on [0, units): within each of the
 // two ranges the first multiple of 8 is dealt XCD by XCD, the rest in order.
+//
+// When every XCD has at least two rounds of full-block units and half a round
+// of pieces, half of its CUs start with pieces instead (an XCD's j-th
+// workgroup: full units 0..15, then pieces 0..15, then the other full units,
+// then the other pieces).  The two halves then reach their unit boundaries at
+// different times, so the bursts of query loads and output stores at those
+// boundaries do not all hit HBM at once; the last workgroup still ends at the
+// same time.
 __device__ __forceinline__ long long unit_of_block(const AttnArgs& a, long long x) {
   constexpr int kXcds = 8;
+  constexpr int kHalfXcd = 16;  // half of one XCD's 32 CUs
   const long long units_full = static_cast<long long>(a.B) * a.full_rb * a.split_full;
+  const long long units = units_full + (a.full_rb < a.n_rb ? static_cast<long long>(a.B) * a.split_tail : 0);
+  const long long n_f = units_full / kXcds;           // full-block units per XCD
+  const long long n_p = (units - units_full) / kXcds;  // pieces per XCD
+  if (units_full % kXcds == 0 && (units - units_full) % kXcds == 0 && n_f >= 2 * kHalfXcd && n_p >= kHalfXcd) {
+    const long long k = x % kXcds;
+    const long long j = x / kXcds;
+    if (j < kHalfXcd) return k * n_f + j;
+    if (j < 2 * kHalfXcd) return units_full + k * n_p + (j - kHalfXcd);
+    if (j < n_f + kHalfXcd) return k * n_f + (j - kHalfXcd);
+    return units_full + k * n_p + (j - n_f);
+  }
   const long long f8 = units_full / kXcds * kXcds;
   if (x < f8) return (x % kXcds) * (f8 / kXcds) + x / kXcds;
   const long long p = x - f8;
-  const long long units = units_full + (a.full_rb < a.n_rb ? static_cast<long long>(a.B) * a.split_tail : 0);
   const long long r8 = (units - f8) / kXcds * kXcds;
   if (p < r8) return f8 + (p % kXcds) * (r8 / kXcds) + p / kXcds;
   return x;
