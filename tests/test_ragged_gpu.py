@@ -99,21 +99,30 @@ def test_ragged_bound_above_lengths():
     _check([9, 20], [300, 64], 8, 512, 64, "bf16", max_q=200, stride_pad=5000)
 
 
-def test_ragged_equal_lengths_match_uniform():
-    """Every request the same size: the ragged call agrees with tv_verify_attn
-    to within rounding (its kv pieces may differ)."""
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_ragged_equal_lengths_match_uniform(dt):
+    """Every request the same size: the ragged call and tv_verify_attn agree.
+    The two plan their kv pieces independently, and the bf16 kernel rounds
+    each weight relative to its piece's reference max, so with the bf16 cache
+    they agree to the bf16 bound (each also against the oracle); with the
+    fp32 cache only the order of float32 sums differs."""
     B, q, P, H = 3, 17, 700, 8
-    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs([q] * B, [P] * B, H, 512, 64, "bf16", 0, seed=9)
+    d_c, d_r = (512, 64) if dt == "bf16" else (256, 64)
+    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs([q] * B, [P] * B, H, d_c, d_r, dt, 0, seed=9)
     sm = 0.0417
-    args = [torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(), _cache(c_kv, "bf16"),
-            _cache(k_rope, "bf16")]
+    args = [torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(), _cache(c_kv, dt), _cache(k_rope, dt)]
     r = tv.verify_attn_ragged(*args, torch.from_numpy(parent).cuda(), torch.full((B,), P, dtype=torch.int32).cuda(),
                               torch.full((B,), q, dtype=torch.int32).cuda(), q, sm)
-    u = tv.verify_attn(args[0].view(B, q, H, 512), args[1].view(B, q, H, 64), args[2], args[3],
+    u = tv.verify_attn(args[0].view(B, q, H, d_c), args[1].view(B, q, H, d_r), args[2], args[3],
                        torch.from_numpy(parent.reshape(B, q)).cuda(), P, sm)
     torch.cuda.synchronize()
-    e = errors(r.cpu().numpy().reshape(B, q, H, 512), u.cpu().numpy())
-    assert e["max_rel"] <= 1e-5, e
+    r, u = r.cpu().numpy().reshape(B, q, H, d_c), u.cpu().numpy()
+    e = errors(r, u)
+    assert e["max_rel"] <= (1e-5 if dt == "f32" else TOL["bf16"]["max_rel"]), e
+    ref, _ = O.verify_attn(O.as_f64(q_lat.reshape(B, q, H, d_c), "f32"), O.as_f64(q_rope.reshape(B, q, H, d_r), "f32"),
+                           O.as_f64(c_kv, dt), O.as_f64(k_rope, dt), parent.reshape(B, q), P, sm)
+    for got in (r, u):
+        assert errors(got, ref)["max_rel"] <= TOL[dt]["max_rel"]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
@@ -156,3 +165,55 @@ def test_ragged_many_row_blocks_tail_pieces():
     q_lens = [int(x) for x in rng.integers(17, 65, size=B)]
     prefixes = [int(x) for x in rng.integers(100, 3000, size=B)]
     _check(q_lens, prefixes, 64, 512, 64, "bf16")
+
+
+@pytest.mark.parametrize("which", ["bench_like", "uniform", "few_long", "many_short", "valu"])
+def test_ragged_records_match_plan_model(which):
+    """The prep kernel's records (plan choice, class order, numbering) equal
+    the host model's word for word, and the attention over them matches the
+    oracle on sampled requests."""
+    import ragged_plan_model as RP
+    rng = np.random.default_rng(zlib.crc32(which.encode()))
+    dt, H, d_c, d_r = "bf16", 16, 512, 64
+    if which == "bench_like":
+        q_lens = [int(x) for x in rng.choice([9, 17, 33], 32)]
+        prefixes = [int(x) for x in rng.integers(2048, 16384, 32)]
+    elif which == "uniform":
+        q_lens, prefixes = [33] * 16, [3000] * 16
+    elif which == "few_long":
+        q_lens, prefixes = [33, 5, 40], [30000, 45000, 12000]
+    elif which == "many_short":
+        q_lens = [int(x) for x in rng.integers(0, 20, 150)]
+        prefixes = [int(x) for x in rng.integers(0, 600, 150)]
+    else:
+        dt, H, d_c, d_r = "f32", 4, 128, 32
+        q_lens = [int(x) for x in rng.integers(1, 70, 12)]
+        prefixes = [int(x) for x in rng.integers(0, 9000, 12)]
+    max_q = max(q_lens)
+    print(f"ragged records {which} B={len(q_lens)}", flush=True)
+    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs(q_lens, prefixes, H, d_c, d_r, dt, 5, seed=1)
+    S = c_kv.shape[1]
+    ws_n = tv.load().tv_verify_attn_ragged_workspace_size(len(q_lens), H, max_q, S, d_c, d_r,
+                                                          tv.TV_BF16 if dt == "bf16" else tv.TV_F32)
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device="cuda")
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    out = tv.verify_attn_ragged(torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(), _cache(c_kv, dt),
+                                _cache(k_rope, dt), torch.from_numpy(parent).cuda(),
+                                torch.tensor(prefixes, dtype=torch.int32).cuda(),
+                                torch.tensor(q_lens, dtype=torch.int32).cuda(), max_q, sm, workspace=ws)
+    torch.cuda.synchronize()
+    rpb, target = (128, 256) if dt == "bf16" and d_c == 512 and d_r == 64 else (16, 512)  # rows per workgroup
+    model = RP.records_words(RP.plan(prefixes, q_lens, H, max_q, S, rpb, target))
+    got = ws[:4 * len(model)].view(torch.int32).cpu().numpy().tolist()
+    assert got == model
+    out = out.cpu().numpy()
+    starts = np.cumsum([0] + q_lens)
+    for b in rng.choice(len(q_lens), size=min(3, len(q_lens)), replace=False):
+        q, P, s = q_lens[b], prefixes[b], starts[b]
+        if q == 0:
+            continue
+        ref, _ = O.verify_attn(O.as_f64(q_lat[None, s:s + q], "f32"), O.as_f64(q_rope[None, s:s + q], "f32"),
+                               O.as_f64(c_kv[b:b + 1, :P + q], dt), O.as_f64(k_rope[b:b + 1, :P + q], dt),
+                               parent[None, s:s + q], P, sm)
+        e = errors(out[s:s + q], ref[0])
+        assert e["max_rel"] <= TOL[dt]["max_rel"], (which, b, e)

@@ -15,7 +15,6 @@ namespace tv {
 namespace {
 constexpr int kNumCU = 256;          // MI355X; fixed so plans depend on shapes only
 constexpr int kMinKeysPerSplit = 256;
-constexpr int kMinKeysPerTailPiece = 1024;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -110,14 +109,12 @@ AttnPlan plan_attention(const AttnShape& s) {
   return p;
 }
 
-// Ragged batch: the same choices as plan_attention, made from upper bounds (B
-// requests of at most max_q_len nodes over at most kv_stride keys).  With too
-// few row blocks to fill the GPU, every row block's kv range is cut into
-// pieces of chunk_full keys (shorter requests get fewer pieces).  Otherwise
-// full row blocks stay whole and the prep kernel cuts each request's partial
-// last row block into as many pieces (at most kMaxTailSplit) as fill the last
-// round of workgroups.  units, n_slots and merge_blocks are upper bounds (the
-// launch sizes); the workspace starts with the request records.
+// Ragged batch: launch sizes from the bounds (B requests of at most max_q_len
+// nodes over at most kv_stride keys); the prep kernel makes the plan from the
+// device lengths.  Partial-result slots are capped at max(2 target,
+// kMaxTailSplit B) (a candidate plan needing more is not taken; cutting
+// nothing needs none).  Every unit is a row block whole or a split piece, so
+// units <= B n_rb + slots; merged blocks <= min(B n_rb, slots / 2).
 AttnPlan plan_attention_ragged(const AttnShape& s) {
   AttnPlan p{};
   const bool mfma = s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
@@ -126,164 +123,275 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
   p.keys_per_tile = mfma ? kMfmaKeys : kValuKeys;
   p.n_rb = ceil_div(static_cast<long long>(s.q_len) * s.H, p.rows_per_block);
   p.full_rb = p.n_rb;
+  p.split_full = p.split_tail = 1;
+  p.chunk_full = p.chunk_tail = s.kv_len;
   p.target = mfma ? kNumCU : 2 * kNumCU;
   const long long blocks = static_cast<long long>(s.B) * p.n_rb;
-  if (blocks < p.target) {
-    cut_for_blocks(s.kv_len, blocks, p.target, p.keys_per_tile, 10, p.split_full, p.chunk_full);
-    p.tail_pieces = false;
-    p.units = blocks * p.split_full;
-    p.n_slots = p.split_full > 1 ? p.units : 0;
-    p.merge_blocks = p.split_full > 1 ? blocks : 0;
-  } else {
-    p.split_full = 1;
-    p.chunk_full = ceil_div(s.kv_len, p.keys_per_tile) * p.keys_per_tile;
-    p.tail_pieces = true;
-    p.units = static_cast<long long>(s.B) * (p.n_rb + kMaxTailSplit);
-    p.n_slots = static_cast<long long>(s.B) * kMaxTailSplit;
-    p.merge_blocks = s.B;
-  }
-  p.split_tail = p.split_full;
-  p.chunk_tail = p.chunk_full;
-  const size_t rec = align256((static_cast<size_t>(s.B) * kReqFields + kReqTotals) * sizeof(int32_t));
-  p.ws_bytes = rec;
-  p.ws_o_off = p.ws_m_off = p.ws_l_off = rec;
-  if (p.n_slots > 0) {
-    const size_t rows = static_cast<size_t>(p.n_slots) * p.rows_per_block;
-    p.ws_m_off = rec + align256(rows * s.d_c * sizeof(float));
-    p.ws_l_off = p.ws_m_off + align256(rows * sizeof(float));
-    p.ws_bytes = p.ws_l_off + align256(rows * sizeof(float));
-  }
+  const long long cap = static_cast<long long>(s.B) * kMaxTailSplit;
+  p.n_slots = 2 * p.target > cap ? 2 * p.target : cap;
+  p.units = blocks + p.n_slots;
+  p.merge_blocks = blocks < p.n_slots / 2 ? blocks : p.n_slots / 2;
+  const size_t rec = align256(req_words(s.B) * sizeof(int32_t));
+  p.ws_o_off = rec;
+  p.ws_m_off = rec + align256(static_cast<size_t>(p.n_slots) * p.rows_per_block * s.d_c * sizeof(float));
+  p.ws_l_off = p.ws_m_off + align256(static_cast<size_t>(p.n_slots) * p.rows_per_block * sizeof(float));
+  p.ws_bytes = p.ws_l_off + align256(static_cast<size_t>(p.n_slots) * p.rows_per_block * sizeof(float));
   return p;
 }
 
 namespace {
 
-static_assert(kMfmaKeys == kValuKeys, "piece sizes of the partial blocks are whole tiles of either kernel");
+static_assert(kMfmaKeys == kPlanTile && kValuKeys == kPlanTile, "plans count tiles of 32 keys for both kernels");
 
-// Request records of a ragged batch (one workgroup of 1024 threads).  Lengths
-// are clamped into the bounds (q_len to [0, max_q], prefix to [0, kv_stride -
-// q_len]).  Per request: full row blocks and their pieces, the pieces of the
-// partial last block, and (exclusive scans over the batch) its first node,
-// full-block unit, partial-block unit, slot and merged block; then the totals.
-struct ReqShape {
-  int q, P, n_full, split, tsplit, tchunk;
+// Lengths of request b clamped into the bounds (q_len to [0, max_q], prefix
+// to [0, kv_stride - q_len]); its row blocks and tiles.
+struct ReqLen {
+  int q, P, nblk, tiles;
 };
-
-__device__ __forceinline__ ReqShape req_shape(const int32_t* prefix_len, const int32_t* q_len, int b, int H, int max_q,
-                                              int kv_stride, int rpb, int chunk, bool tail_pieces, int g_tsplit) {
-  ReqShape r;
+__device__ __forceinline__ ReqLen req_len(const int32_t* prefix_len, const int32_t* q_len, int b, int H, int max_q,
+                                          int kv_stride, int rpb) {
+  ReqLen r;
   r.q = min(max(q_len[b], 0), max_q);
   r.P = min(max(prefix_len[b], 0), kv_stride - r.q);
-  const int R = r.q * H;
-  const int kv = r.P + r.q;
-  r.n_full = R / rpb;
-  r.split = tail_pieces ? 1 : max((kv + chunk - 1) / chunk, 1);
-  r.tsplit = 0;
-  r.tchunk = 0;
-  if (R % rpb != 0) {
-    if (!tail_pieces) {
-      r.tsplit = r.split;
-      r.tchunk = chunk;
-    } else {
-      // Pieces of at least kMinKeysPerTailPiece keys: a unit's set-up (~10
-      // tile-steps) should stay small next to its sweep.
-      const int want = min(g_tsplit, max(1, kv / kMinKeysPerTailPiece));
-      r.tchunk = (((kv + want - 1) / want + kMfmaKeys - 1) / kMfmaKeys) * kMfmaKeys;  // whole tiles (both kernels: 32 keys)
-      r.tsplit = (kv + r.tchunk - 1) / r.tchunk;
-    }
-  }
+  r.nblk = (r.q * H + rpb - 1) / rpb;
+  r.tiles = (r.P + r.q + kPlanTile - 1) / kPlanTile;
   return r;
 }
 
-__global__ __launch_bounds__(1024) void ragged_prep_kernel(const int32_t* __restrict__ prefix_len,
-                                                           const int32_t* __restrict__ q_len, int B, int H,
-                                                           int max_q, int kv_stride, int rpb, int chunk,
-                                                           int tail_pieces, int target, int32_t* __restrict__ rq) {
-  constexpr int kN = 5;  // nodes, full-block units, partial-block units, slots, merged blocks
-  __shared__ int s_scan[kN][1024];
-  __shared__ int s_tsplit;
-  const int t = threadIdx.x;
-  const int per = (B + 1023) / 1024;
-  const int b0 = min(B, t * per);
-  const int b1 = min(B, b0 + per);
-  // Pieces of the partial blocks: fill what the full blocks leave of their
-  // last round (a round more if that is less than one piece per block).
-  int g_tsplit = 1;
-  if (tail_pieces) {
-    int full = 0, part = 0;
-    for (int b = b0; b < b1; ++b) {
-      const ReqShape r = req_shape(prefix_len, q_len, b, H, max_q, kv_stride, rpb, chunk, false, 1);
-      full += r.n_full;
-      part += r.tsplit > 0;
-    }
-    s_scan[0][t] = full;
-    s_scan[1][t] = part;
-    __syncthreads();
-    for (int off = 512; off > 0; off >>= 1) {
-      if (t < off) {
-        s_scan[0][t] += s_scan[0][t + off];
-        s_scan[1][t] += s_scan[1][t + off];
-      }
-      __syncthreads();
-    }
-    if (t == 0) {
-      const int n_part = s_scan[1][0];
-      int free_slots = target - s_scan[0][0] % target;
-      if (free_slots < n_part) free_slots += target;
-      s_tsplit = min(max(free_slots / max(n_part, 1), 1), kMaxTailSplit);
-    }
-    __syncthreads();
-    g_tsplit = s_tsplit;
-    __syncthreads();
-  }
-  int sum[kN] = {0, 0, 0, 0, 0};
-  for (int b = b0; b < b1; ++b) {
-    const ReqShape r = req_shape(prefix_len, q_len, b, H, max_q, kv_stride, rpb, chunk, tail_pieces, g_tsplit);
-    sum[0] += r.q;
-    sum[1] += r.n_full * r.split;
-    sum[2] += r.tsplit;
-    sum[3] += (r.split > 1 ? r.n_full * r.split : 0) + (r.tsplit > 1 ? r.tsplit : 0);
-    sum[4] += (r.split > 1 ? r.n_full : 0) + (r.tsplit > 1 ? 1 : 0);
-  }
-#pragma unroll
-  for (int k = 0; k < kN; ++k) s_scan[k][t] = sum[k];
+constexpr int kPrepThreads = 1024;
+constexpr int kSortMax = 4096;  // classes sorted in LDS (B <= 2048); larger batches keep request order
+
+// Sum over the workgroup (ends with every thread holding the total).
+__device__ long long block_sum(long long v, long long* s_part) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int wave = threadIdx.x >> 6;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v[kN];
-#pragma unroll
-    for (int k = 0; k < kN; ++k) v[k] = t >= off ? s_scan[k][t - off] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kN; ++k) s_scan[k][t] += v[k];
-    __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_part[wave] = v;
+  __syncthreads();
+  long long t = 0;
+  for (int i = 0; i < kPrepThreads / 64; ++i) t += s_part[i];
+  return t;
+}
+
+// Exclusive scan over the workgroup of one value per thread (wave scans by
+// shuffles, then the 16 wave totals); returns this thread's offset; *total
+// gets the sum.
+__device__ int block_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  int run[kN];
-#pragma unroll
-  for (int k = 0; k < kN; ++k) run[k] = s_scan[k][t] - sum[k];
+  __syncthreads();
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < kPrepThreads / 64; ++w) {
+    const int sw = s_wave[w];
+    before += w < wave ? sw : 0;
+    tot += sw;
+  }
+  *total = tot;
+  return before + x - v;
+}
+
+// The records of a ragged batch (one workgroup of 1024 threads):
+//  1. T0 = sum over requests of row blocks x (tiles + set-up) / target;
+//  2. for every candidate cut (plan_caps): units, pieces, shortest and
+//     longest unit and a histogram of unit costs; the candidate with the
+//     least plan_estimate among those within the slot budget is taken;
+//  3. the requests' two classes are sorted by piece length, longest first
+//     (ties by class id), and numbered in that order; nodes, slots and merged
+//     blocks are numbered request by request.
+__global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t* __restrict__ prefix_len,
+                                                                   const int32_t* __restrict__ q_len, int B, int H,
+                                                                   int max_q, int kv_stride, int rpb, int target,
+                                                                   int max_slots, int32_t* __restrict__ rq) {
+  __shared__ long long s_part[kPrepThreads / 64];
+  __shared__ unsigned long long s_units[kPlanCands], s_pieces[kPlanCands];
+  __shared__ int s_dmin[kPlanCands], s_dmax[kPlanCands];
+  __shared__ int s_hist[kPlanCands][64];
+  __shared__ double s_est[kPlanCands];
+  __shared__ int s_capb[kPlanCands], s_capt[kPlanCands];
+  __shared__ int s_choice;
+  __shared__ int s_scan[kPrepThreads / 64];
+  __shared__ unsigned long long s_sort[kSortMax];
+  const int t = threadIdx.x;
+  const int per = (B + kPrepThreads - 1) / kPrepThreads;
+  const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+
+  long long w0 = 0, wt = 0;
   for (int b = b0; b < b1; ++b) {
-    const ReqShape r = req_shape(prefix_len, q_len, b, H, max_q, kv_stride, rpb, chunk, tail_pieces, g_tsplit);
+    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    w0 += static_cast<long long>(r.nblk) * (r.tiles + kPlanSetupTiles);
+    wt += static_cast<long long>(r.nblk) * r.tiles;
+  }
+  const long long T0 = max(1ll, block_sum(w0, s_part) / target);
+  const long long Wt = block_sum(wt, s_part);
+
+  for (int i = t; i < kPlanCands * 64; i += kPrepThreads) (&s_hist[0][0])[i] = 0;
+  if (t < kPlanCands) {
+    s_units[t] = s_pieces[t] = 0;
+    s_dmin[t] = INT_MAX;
+    s_dmax[t] = 0;
+    plan_caps(T0, t, s_capb[t], s_capt[t]);
+  }
+  __syncthreads();
+  // One (request, candidate) pair per thread at a time.
+  for (int i = t; i < B * kPlanCands; i += kPrepThreads) {
+    const int b = i / kPlanCands, c = i - b * kPlanCands;
+    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    if (r.nblk == 0) continue;
+    const ReqCut k = cut_request(r.tiles, s_capb[c], s_capt[c]);
+    const int last_b = r.tiles - (k.n_body - 1) * k.c_body, last_t = r.tiles - (k.n_tail - 1) * k.c_tail;
+    const int nb = r.nblk - 1;
+    const unsigned long long units = static_cast<unsigned long long>(nb) * k.n_body + k.n_tail;
+    const unsigned long long pieces =
+        (k.n_body > 1 ? static_cast<unsigned long long>(nb) * k.n_body : 0ull) + (k.n_tail > 1 ? k.n_tail : 0);
+    atomicAdd(&s_units[c], units);
+    if (pieces) atomicAdd(&s_pieces[c], pieces);
+    atomicMin(&s_dmin[c], min(nb ? last_b : INT_MAX, last_t) + kPlanSetupTiles);
+    atomicMax(&s_dmax[c], max(nb ? k.c_body : 0, k.c_tail) + kPlanSetupTiles);
+    // (counts of candidates past the slot budget may wrap; those are never read)
+    if (nb) {
+      if (k.n_body > 1) atomicAdd(&s_hist[c][plan_bucket(k.c_body + kPlanSetupTiles)], nb * (k.n_body - 1));
+      atomicAdd(&s_hist[c][plan_bucket(last_b + kPlanSetupTiles)], nb);
+    }
+    if (k.n_tail > 1) atomicAdd(&s_hist[c][plan_bucket(k.c_tail + kPlanSetupTiles)], k.n_tail - 1);
+    atomicAdd(&s_hist[c][plan_bucket(last_t + kPlanSetupTiles)], 1);
+  }
+  __syncthreads();
+  if (t < kPlanCands) {
+    const long long units = static_cast<long long>(s_units[t]);
+    s_est[t] = static_cast<long long>(s_pieces[t]) > max_slots || units == 0
+                   ? (t == 0 ? 0.0 : -1.0)
+                   : plan_estimate(Wt + kPlanSetupTiles * units, units, s_dmin[t], s_dmax[t],
+                                   static_cast<long long>(s_pieces[t]), s_hist[t], target);
+  }
+  __syncthreads();
+  if (t == 0) {
+    int best = 0;
+    for (int c = 1; c < kPlanCands; ++c)
+      if (s_est[c] >= 0.0 && s_est[c] < s_est[best]) best = c;
+    s_choice = best;
+  }
+  __syncthreads();
+  const int cap_b = s_capb[s_choice], cap_t = s_capt[s_choice];
+
+  // Per request: nodes, slots, merged blocks (request order).
+  int n_q = 0, n_slot = 0, n_merge = 0;
+  for (int b = b0; b < b1; ++b) {
+    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    if (r.nblk == 0) continue;
+    const ReqCut k = cut_request(r.tiles, cap_b, cap_t);
+    n_q += r.q;
+    n_slot += (k.n_body > 1 ? (r.nblk - 1) * k.n_body : 0) + (k.n_tail > 1 ? k.n_tail : 0);
+    n_merge += (k.n_body > 1 ? r.nblk - 1 : 0) + (k.n_tail > 1 ? 1 : 0);
+  }
+  int tot_q, tot_slot, tot_merge;
+  int o_q = block_scan(n_q, s_scan, &tot_q);
+  int o_slot = block_scan(n_slot, s_scan, &tot_slot);
+  int o_merge = block_scan(n_merge, s_scan, &tot_merge);
+  for (int b = b0; b < b1; ++b) {
+    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    ReqCut k{1, r.tiles, 1, r.tiles};
+    if (r.nblk > 0) k = cut_request(r.tiles, cap_b, cap_t);
     int32_t* o = rq + b * kReqFields;
-    o[kReqQStart] = run[0];
+    o[kReqQStart] = o_q;
     o[kReqQLen] = r.q;
     o[kReqPrefix] = r.P;
-    o[kReqNFull] = r.n_full;
-    o[kReqSplit] = r.split;
-    o[kReqTSplit] = r.tsplit;
-    o[kReqTChunk] = r.tchunk;
-    o[kReqFull0] = run[1];
-    o[kReqTail0] = run[2];
-    o[kReqSlot0] = run[3];
-    o[kReqMerge0] = run[4];
-    run[0] += r.q;
-    run[1] += r.n_full * r.split;
-    run[2] += r.tsplit;
-    run[3] += (r.split > 1 ? r.n_full * r.split : 0) + (r.tsplit > 1 ? r.tsplit : 0);
-    run[4] += (r.split > 1 ? r.n_full : 0) + (r.tsplit > 1 ? 1 : 0);
+    o[kReqNBlk] = r.nblk;
+    o[kReqBSplit] = k.n_body;
+    o[kReqBChunk] = k.c_body * kPlanTile;
+    o[kReqTSplit] = k.n_tail;
+    o[kReqTChunk] = k.c_tail * kPlanTile;
+    o[kReqSlot0] = o_slot;
+    o[kReqMerge0] = o_merge;
+    if (r.nblk > 0) {
+      o_q += r.q;
+      o_slot += (k.n_body > 1 ? (r.nblk - 1) * k.n_body : 0) + (k.n_tail > 1 ? k.n_tail : 0);
+      o_merge += (k.n_body > 1 ? r.nblk - 1 : 0) + (k.n_tail > 1 ? 1 : 0);
+    }
   }
-  if (t == 1023) {
-    rq[B * kReqFields] = s_scan[1][1023];
-    rq[B * kReqFields + 1] = s_scan[1][1023] + s_scan[2][1023];
-    rq[B * kReqFields + 2] = s_scan[4][1023];
+
+  // Classes in launch order: longest piece first, ties by id; classes with no
+  // units last.  Without the sort (very large batches) request order.
+  const int n_cls = 2 * B;
+  const bool sorted = n_cls <= kSortMax;
+  auto cls_of = [&](int id, int& units, int& len) {
+    const ReqLen r = req_len(prefix_len, q_len, id >> 1, H, max_q, kv_stride, rpb);
+    units = 0;
+    len = 0;
+    if (r.nblk == 0) return;
+    const ReqCut k = cut_request(r.tiles, cap_b, cap_t);
+    if (id & 1) {
+      units = k.n_tail;
+      len = k.c_tail;
+    } else if (r.nblk > 1) {
+      units = (r.nblk - 1) * k.n_body;
+      len = k.c_body;
+    }
+  };
+  int n_sort = 1;
+  if (sorted) {
+    while (n_sort < n_cls) n_sort <<= 1;
+    for (int i = t; i < n_sort; i += kPrepThreads) {
+      unsigned long long key = ~0ull;
+      if (i < n_cls) {
+        int units, len;
+        cls_of(i, units, len);
+        key = (static_cast<unsigned long long>(0xffffffffu - static_cast<unsigned>(units ? len : 0)) << 32) |
+              static_cast<unsigned>(i);
+      }
+      s_sort[i] = key;
+    }
+    __syncthreads();
+    for (int k = 2; k <= n_sort; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = t; i < n_sort; i += kPrepThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const unsigned long long x = s_sort[i], y = s_sort[l];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) {
+              s_sort[i] = y;
+              s_sort[l] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  // Number the units class by class in launch order: thread t takes a
+  // contiguous run of positions.
+  const int cper = (n_cls + kPrepThreads - 1) / kPrepThreads;
+  const int p0 = min(n_cls, t * cper), p1 = min(n_cls, p0 + cper);
+  int n_u = 0;
+  for (int p = p0; p < p1; ++p) {
+    const int id = sorted ? static_cast<int>(s_sort[p] & 0xffffffffu) : p;
+    int units, len;
+    cls_of(id, units, len);
+    n_u += units;
+  }
+  int tot_units;
+  int o_u = block_scan(n_u, s_scan, &tot_units);
+  int32_t* cu0 = rq + B * kReqFields;
+  int32_t* cid = cu0 + 2 * B;
+  for (int p = p0; p < p1; ++p) {
+    const int id = sorted ? static_cast<int>(s_sort[p] & 0xffffffffu) : p;
+    int units, len;
+    cls_of(id, units, len);
+    cu0[p] = o_u;
+    cid[p] = id;
+    o_u += units;
+  }
+  if (t == 0) {
+    int32_t* tot = cid + 2 * B;
+    tot[kTotUnits] = tot_units;
+    tot[kTotMerge] = tot_merge;
+    tot[kTotChoice] = s_choice;
   }
 }
 
@@ -292,34 +400,29 @@ __global__ __launch_bounds__(1024) void ragged_prep_kernel(const int32_t* __rest
 // Combine the pieces of split row blocks: w_s = l_s * exp(m_s - max m),
 // out = sum w_s o_s / sum w_s, lse = max m + log(sum w_s).
 // One thread per (merged row block, row, float4 column).
-// n_blocks: merged row blocks launched (for a ragged batch an upper bound;
-// blocks past the batch's total return at once).
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, long long n_blocks) {
+__device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long idx) {
   const int cpt = d_c / 4;
   const int rpb = a.rows_per_block;
   const long long full_blocks = a.split_full > 1 ? static_cast<long long>(a.B) * a.full_rb : 0;
-  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= n_blocks * rpb * cpt) return;
   const int col4 = static_cast<int>(idx % cpt);
   const int r = static_cast<int>((idx / cpt) % rpb);
   const long long mb = idx / (static_cast<long long>(cpt) * rpb);
   int rb, n_split, R;
   long long slot0, row0;
   if (a.req) {
-    if (mb >= a.req[a.B * kReqFields + 2]) return;
     const int bq = find_request(a.req, a.B, kReqMerge0, mb);
     const int32_t* rec = a.req + bq * kReqFields;
     const int m = static_cast<int>(mb - rec[kReqMerge0]);
-    const int split = rec[kReqSplit];
-    const int full_merges = split > 1 ? rec[kReqNFull] : 0;
-    if (m < full_merges) {  // a full row block
+    const int bsplit = rec[kReqBSplit];
+    const int body_merges = bsplit > 1 ? rec[kReqNBlk] - 1 : 0;
+    if (m < body_merges) {  // a row block before the last
       rb = m;
-      n_split = split;
-      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(m) * split;
-    } else {  // the partial last row block
-      rb = rec[kReqNFull];
+      n_split = bsplit;
+      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(m) * bsplit;
+    } else {  // the last row block
+      rb = rec[kReqNBlk] - 1;
       n_split = rec[kReqTSplit];
-      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(full_merges) * split;
+      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(body_merges) * bsplit;
     }
     R = rec[kReqQLen] * a.H;
     row0 = static_cast<long long>(rec[kReqQStart]) * a.H;
@@ -380,21 +483,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, lo
   if (col4 == 0 && a.lse) a.lse[grow] = M + logf(W);
 }
 
+// n_blocks: merged row blocks of a uniform batch; a ragged batch's count is
+// read from its records.  The grid strides over the work.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, long long n_blocks) {
+  if (a.req) n_blocks = req_totals(a.req, a.B)[kTotMerge];
+  const long long total = n_blocks * a.rows_per_block * (d_c / 4);
+  const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  for (long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride)
+    merge_one(a, d_c, idx);
+}
+
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
   hipError_t e = plan.kernel == AttnKernel::kMfmaBf16 ? launch_attn_mfma_bf16(s, plan, a, stream)
                                                        : launch_attn_valu(s, plan, a, stream);
   if (e != hipSuccess || plan.merge_blocks == 0) return e;
   const long long total = plan.merge_blocks * plan.rows_per_block * (s.d_c / 4);
-  attn_merge_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), 256, 0, stream>>>(a, s.d_c,
-                                                                                           plan.merge_blocks);
+  long long grid = (total + 255) / 256;
+  if (a.req && grid > 8 * kNumCU) grid = 8 * kNumCU;  // ragged: an upper bound; the grid strides
+  attn_merge_kernel<<<dim3(static_cast<unsigned>(grid)), 256, 0, stream>>>(a, s.d_c, plan.merge_blocks);
   return hipGetLastError();
 }
 
 hipError_t launch_ragged_prep(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, const int32_t* prefix_len,
                               const int32_t* q_len, hipStream_t stream) {
-  ragged_prep_kernel<<<dim3(1), 1024, 0, stream>>>(prefix_len, q_len, s.B, s.H, s.q_len, s.kv_len,
-                                                   plan.rows_per_block, plan.chunk_full, plan.tail_pieces ? 1 : 0,
-                                                   static_cast<int>(plan.target), const_cast<int32_t*>(a.req));
+  ragged_prep_kernel<<<dim3(1), kPrepThreads, 0, stream>>>(prefix_len, q_len, s.B, s.H, s.q_len, s.kv_len,
+                                                           plan.rows_per_block, static_cast<int>(plan.target),
+                                                           static_cast<int>(plan.n_slots), const_cast<int32_t*>(a.req));
   return hipGetLastError();
 }
 

@@ -140,7 +140,6 @@ tv_status_t ragged_args(const float* q_lat, const float* q_rope, const void* c_k
   a.chunk_tail = plan.chunk_tail;
   a.sm_scale = sm_scale;
   a.kv_stride = kv_stride;
-  a.chunk = plan.chunk_full;
   return TV_OK;
 }
 

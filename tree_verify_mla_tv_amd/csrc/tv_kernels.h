@@ -70,7 +70,6 @@ struct AttnPlan {
   int split_tail, chunk_tail;  // meaningful when full_rb < n_rb
   long long units;
   long long target;            // workgroups that run at once (ragged plans)
-  bool tail_pieces;            // ragged: cut the partial last row blocks into pieces on the device
   long long n_slots;           // partial-result slots in the workspace
   long long merge_blocks;      // row blocks that need merging
   size_t ws_bytes;
@@ -104,31 +103,122 @@ struct AttnArgs {
   // request records the prep kernel wrote (null for a uniform batch).
   const int32_t* req;
   int kv_stride;  // cache rows per request
-  int chunk;      // keys per kv piece
 };
 
-// Request record of a ragged batch: [B][kReqFields] int32, then kReqTotals
-// totals (units of full row blocks, all units, merged blocks).  Units of full
-// row blocks come first in launch order, request by request; the pieces of
-// the partial last row blocks after them.
+// Records of a ragged batch, written by the prep kernel into the workspace
+// (int32): [B][kReqFields] per request, then the request's two classes of
+// units in launch order -- first unit cls_u0[2B] and class id cls_id[2B]
+// (2b: the row blocks before the last, 2b + 1: the last row block) -- then
+// kReqTotals totals.  A class is every (row block, kv piece) unit of those
+// blocks; its pieces are equal but the last.  Classes run longest piece
+// first.
 enum ReqField : int {
   kReqQStart = 0,  // first node of the request in the packed node arrays
   kReqQLen,        // nodes (0 .. max_q_len)
   kReqPrefix,      // prefix rows
-  kReqNFull,       // full row blocks
-  kReqSplit,       // kv pieces per full row block
-  kReqTSplit,      // kv pieces of the partial last row block (0: no such block)
-  kReqTChunk,      // keys per piece of the partial block
-  kReqFull0,       // first unit of the full blocks
-  kReqTail0,       // first unit of the partial block, counted from the end of all full-block units
+  kReqNBlk,        // row blocks (the last may be partial); 0 when q_len is 0
+  kReqBSplit,      // kv pieces per row block before the last
+  kReqBChunk,      // keys per such piece
+  kReqTSplit,      // kv pieces of the last row block
+  kReqTChunk,      // keys per such piece
   kReqSlot0,       // first partial-result slot
   kReqMerge0,      // first merged row block
   kReqFields
 };
-constexpr int kReqTotals = 3;
-// Most pieces the partial last row block of a request is cut into (to fill
-// the last round of workgroups).
+enum ReqTotal : int { kTotUnits = 0, kTotMerge, kTotChoice, kReqTotals };
+
+__host__ __device__ inline const int32_t* req_cls_u0(const int32_t* rq, int B) { return rq + B * kReqFields; }
+__host__ __device__ inline const int32_t* req_cls_id(const int32_t* rq, int B) { return rq + B * kReqFields + 2 * B; }
+__host__ __device__ inline const int32_t* req_totals(const int32_t* rq, int B) {
+  return rq + B * kReqFields + 4 * B;
+}
+__host__ __device__ inline size_t req_words(int B) { return static_cast<size_t>(B) * (kReqFields + 4) + kReqTotals; }
+
+// Planning of a ragged batch, in tiles of 32 keys (both kernels' tile).  A
+// unit costs its tiles plus kPlanSetupTiles (tree masks, queries, first tile,
+// output).  Candidate plans cap the pieces of the row blocks before the last
+// at cap_body tiles and those of the last block at cap_tail (at most
+// kMaxTailSplit pieces, but never fewer than the other blocks get): the last
+// blocks' shorter pieces fill the gaps the longer units leave.  Candidate 0
+// cuts nothing; the others take cap_body = T0 x {2/3, 1, 1/2, 1/4} and
+// cap_tail = cap_body / {1, 2, 4, 8, 16}, T0 = the whole batch's cost per
+// concurrent workgroup.
+constexpr int kPlanTile = 32;
+constexpr int kPlanSetupTiles = 10;
+constexpr int kMinPieceTiles = 8;
 constexpr int kMaxTailSplit = 16;
+constexpr int kPlanBody = 4, kPlanTail = 5;
+constexpr int kPlanCands = 1 + kPlanBody * kPlanTail;
+
+// Caps of candidate c given T0 (tiles); at most kPlanNoCut, which no request
+// reaches (tiles < 2^26), so larger caps cut nothing either.
+constexpr int kPlanNoCut = 1 << 30;
+__host__ __device__ inline void plan_caps(long long T0, int c, int& cap_body, int& cap_tail) {
+  if (c == 0) {
+    cap_body = cap_tail = kPlanNoCut;
+    return;
+  }
+  const int i = (c - 1) / kPlanTail, j = (c - 1) % kPlanTail;
+  const long long num = i == 0 ? 2 : 1;
+  const long long den = i == 0 ? 3 : (1 << (i - 1));
+  long long body = (T0 < kPlanNoCut ? T0 : kPlanNoCut) * num / den;
+  long long tail = body >> j;
+  body = body < kMinPieceTiles ? kMinPieceTiles : (body > kPlanNoCut ? kPlanNoCut : body);
+  tail = tail < kMinPieceTiles ? kMinPieceTiles : tail;
+  cap_body = static_cast<int>(body);
+  cap_tail = static_cast<int>(tail);
+}
+
+// One request's cut under caps (cap_body, cap_tail): pieces and tiles per
+// piece for the row blocks before the last (n_body, c_body) and for the last
+// (n_tail, c_tail).  1 <= tiles < 2^26.
+struct ReqCut {
+  int n_body, c_body, n_tail, c_tail;
+};
+__host__ __device__ inline ReqCut cut_request(int tiles, int cap_body, int cap_tail) {
+  const unsigned t = static_cast<unsigned>(tiles);
+  ReqCut r;
+  unsigned n = (t + cap_body - 1u) / static_cast<unsigned>(cap_body);
+  r.c_body = static_cast<int>((t + n - 1u) / n);
+  r.n_body = static_cast<int>((t + r.c_body - 1u) / static_cast<unsigned>(r.c_body));
+  n = (t + cap_tail - 1u) / static_cast<unsigned>(cap_tail);
+  n = n < kMaxTailSplit ? n : kMaxTailSplit;
+  n = n > static_cast<unsigned>(r.n_body) ? n : static_cast<unsigned>(r.n_body);
+  r.c_tail = static_cast<int>((t + n - 1u) / n);
+  r.n_tail = static_cast<int>((t + r.c_tail - 1u) / static_cast<unsigned>(r.c_tail));
+  return r;
+}
+
+// Histogram bucket of a unit's cost (>= 1 tile): 4 buckets per octave.
+__host__ __device__ inline int plan_bucket(int t) {
+  const int e = 31 - __builtin_clz(static_cast<unsigned>(t));
+  const int k = 4 * e + ((static_cast<unsigned>(t) << 2 >> e) & 3);
+  return k < 63 ? k : 63;
+}
+__host__ __device__ inline long long plan_bucket_lo(int k) { return (static_cast<long long>(4 + (k & 3)) << (k >> 2)) >> 2; }
+
+// Estimated span of a candidate, in tile-steps: the work per workgroup plus
+// half the shortest unit (the last units fill gaps), at least the longest
+// unit, and with more units than workgroups at least the longest unit plus the
+// (M+1)-th longest (some workgroup runs two); plus the merge pass, about one
+// tile-step of the whole GPU per 16 pieces.
+__host__ __device__ inline double plan_estimate(long long work, long long units, long long d_min, long long d_max,
+                                                long long pieces, const int* hist, long long M) {
+  double e = static_cast<double>(work) / M + 0.5 * d_min;
+  e = e > d_max ? e : static_cast<double>(d_max);
+  if (units > M) {
+    long long cum = 0;
+    for (int k = 63; k >= 0; --k) {
+      cum += hist[k];
+      if (cum >= M + 1) {
+        const double two = static_cast<double>(d_max + plan_bucket_lo(k));
+        e = e > two ? e : two;
+        break;
+      }
+    }
+  }
+  return e + pieces / 16.0;
+}
 
 // The work of one unit (one workgroup), with the shape of its request.
 struct Unit {
@@ -216,7 +306,7 @@ __device__ __forceinline__ long long unit_of_block(const AttnArgs& a, long long 
 // Last request whose first entry in column `field` is <= v (requests with
 // nothing to do share that entry with the next one, so the search lands on the
 // request that owns v).
-__device__ __forceinline__ int find_request(const int32_t* rq, int B, int field, long long v) {
+__host__ __device__ inline int find_request(const int32_t* rq, int B, int field, long long v) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -227,46 +317,50 @@ __device__ __forceinline__ int find_request(const int32_t* rq, int B, int field,
 }
 
 // Ragged batch: block x of the launch (an upper bound of units) -> its unit,
-// or false past the batch's real total.  The real units are dealt to the XCDs
-// as unit_of_block deals a uniform batch's (full-block units, then pieces).
-__device__ __forceinline__ bool decode_unit_ragged(const AttnArgs& a, long long x, Unit& w) {
+// or false past the batch's real total.  Units are numbered class by class in
+// launch order (longest pieces first), so the longest units start first and
+// the short ones fill in at the end.  Within the class of the blocks before
+// the last, unit = piece * (blocks) + block: the row blocks reading one kv
+// piece are neighbours.  Runs of kDealGroup consecutive units go to one XCD
+// (workgroup x runs on XCD x % 8), so neighbours share that XCD's L2.
+constexpr int kDealGroup = 8;
+__host__ __device__ inline bool decode_unit_ragged(const AttnArgs& a, long long x, Unit& w) {
   const int32_t* rq = a.req;
-  const long long u_full = rq[a.B * kReqFields];
-  const long long total = rq[a.B * kReqFields + 1];
+  const int32_t* u0 = req_cls_u0(rq, a.B);
+  const long long total = req_totals(rq, a.B)[kTotUnits];
   if (x >= total) return false;
-  constexpr int kXcds = 8;
-  const long long f8 = u_full / kXcds * kXcds;
-  long long u = x;
-  if (x < f8) {
-    u = (x % kXcds) * (f8 / kXcds) + x / kXcds;
-  } else {
-    const long long p = x - f8;
-    const long long r8 = (total - f8) / kXcds * kXcds;
-    if (p < r8) u = f8 + (p % kXcds) * (r8 / kXcds) + p / kXcds;
+  {
+    constexpr int kXcds = 8, kGroup = kDealGroup;
+    const long long whole = total / (kXcds * kGroup) * (kXcds * kGroup);
+    if (x < whole) {
+      const long long k = x % kXcds, j = x / kXcds;
+      x = (j / kGroup) * (kXcds * kGroup) + k * kGroup + j % kGroup;
+    }
   }
-  int b, chunk;
-  const int32_t* r;
-  if (u < u_full) {
-    b = find_request(rq, a.B, kReqFull0, u);
-    r = rq + b * kReqFields;
-    const int local = static_cast<int>(u - r[kReqFull0]);
-    const int n_full = r[kReqNFull];
-    const int n_split = r[kReqSplit];
-    w.rb = local % n_full;
-    w.split = local / n_full;
-    chunk = a.chunk;
-    w.slot = n_split > 1 ? static_cast<long long>(r[kReqSlot0]) + static_cast<long long>(w.rb) * n_split + w.split
-                         : -1;
+  int lo = 0, hi = 2 * a.B - 1;  // last class whose first unit is <= x (empty classes come last)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (u0[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  const int id = req_cls_id(rq, a.B)[lo];
+  const int local = static_cast<int>(x - u0[lo]);
+  const int b = id >> 1;
+  const int32_t* r = rq + b * kReqFields;
+  const int n_before = r[kReqNBlk] - 1;
+  const int bsplit = r[kReqBSplit];
+  int chunk;
+  if ((id & 1) == 0) {
+    w.rb = local % n_before;
+    w.split = local / n_before;
+    chunk = r[kReqBChunk];
+    w.slot = bsplit > 1 ? static_cast<long long>(r[kReqSlot0]) + static_cast<long long>(w.rb) * bsplit + w.split : -1;
   } else {
-    b = find_request(rq, a.B, kReqTail0, u - u_full);
-    r = rq + b * kReqFields;
-    const int piece = static_cast<int>(u - u_full - r[kReqTail0]);
-    const int n_split = r[kReqSplit];
-    const long long full_slots = n_split > 1 ? static_cast<long long>(r[kReqNFull]) * n_split : 0;
-    w.rb = r[kReqNFull];
-    w.split = piece;
+    w.rb = n_before;
+    w.split = local;
     chunk = r[kReqTChunk];
-    w.slot = r[kReqTSplit] > 1 ? r[kReqSlot0] + full_slots + piece : -1;
+    const long long before = bsplit > 1 ? static_cast<long long>(n_before) * bsplit : 0;
+    w.slot = r[kReqTSplit] > 1 ? r[kReqSlot0] + before + local : -1;
   }
   w.b = b;
   w.q_len = r[kReqQLen];
@@ -274,7 +368,7 @@ __device__ __forceinline__ bool decode_unit_ragged(const AttnArgs& a, long long 
   w.R = w.q_len * a.H;
   w.kv_len = w.P + w.q_len;
   w.k_begin = w.split * chunk;
-  w.k_end = min(w.kv_len, w.k_begin + chunk);
+  w.k_end = w.kv_len < w.k_begin + chunk ? w.kv_len : w.k_begin + chunk;
   w.row0 = static_cast<long long>(r[kReqQStart]) * a.H;
   w.par0 = r[kReqQStart];
   w.kv_row0 = static_cast<long long>(b) * a.kv_stride;
