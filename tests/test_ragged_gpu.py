@@ -217,3 +217,39 @@ def test_ragged_records_match_plan_model(which):
                                parent[None, s:s + q], P, sm)
         e = errors(out[s:s + q], ref[0])
         assert e["max_rel"] <= TOL[dt]["max_rel"], (which, b, e)
+
+
+def test_ragged_records_unsorted_large_batch():
+    """More than 2048 requests: the prep kernel keeps request order (no sort
+    in LDS); its records still equal the model's and every sampled request
+    matches the oracle."""
+    import ragged_plan_model as RP
+    rng = np.random.default_rng(2100)
+    B, H, d_c, d_r = 2100, 2, 512, 64
+    q_lens = [int(x) for x in rng.integers(0, 6, B)]
+    prefixes = [int(x) for x in rng.integers(0, 100, B)]
+    print(f"ragged unsorted B={B}", flush=True)
+    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs(q_lens, prefixes, H, d_c, d_r, "bf16", 0, seed=4)
+    S = c_kv.shape[1]
+    ws_n = tv.load().tv_verify_attn_ragged_workspace_size(B, H, max(q_lens), S, d_c, d_r, tv.TV_BF16)
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device="cuda")
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    out = tv.verify_attn_ragged(torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(), _cache(c_kv, "bf16"),
+                                _cache(k_rope, "bf16"), torch.from_numpy(parent).cuda(),
+                                torch.tensor(prefixes, dtype=torch.int32).cuda(),
+                                torch.tensor(q_lens, dtype=torch.int32).cuda(), max(q_lens), sm, workspace=ws)
+    torch.cuda.synchronize()
+    model = RP.plan(prefixes, q_lens, H, max(q_lens), S, 128, 256)
+    assert model["cls_id"] == list(range(2 * B))
+    words = RP.records_words(model)
+    assert ws[:4 * len(words)].view(torch.int32).cpu().numpy().tolist() == words
+    out = out.cpu().numpy()
+    starts = np.cumsum([0] + q_lens)
+    for b in rng.choice(B, size=12, replace=False):
+        q, P, s = q_lens[b], prefixes[b], starts[b]
+        if q == 0:
+            continue
+        ref, _ = O.verify_attn(O.as_f64(q_lat[None, s:s + q], "f32"), O.as_f64(q_rope[None, s:s + q], "f32"),
+                               O.as_f64(c_kv[b:b + 1, :P + q], "bf16"), O.as_f64(k_rope[b:b + 1, :P + q], "bf16"),
+                               parent[None, s:s + q], P, sm)
+        assert errors(out[s:s + q], ref[0])["max_rel"] <= TOL["bf16"]["max_rel"], b
