@@ -267,7 +267,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-sample", type=int, default=6, help="trees the CPU oracle times (0 = skip)")
     ap.add_argument("--no-next-rows", dest="next_rows", action="store_false",
