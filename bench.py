@@ -373,6 +373,8 @@ def main() -> int:
             "frac": round(achieved_tflops / peak, 4),
             "traffic": traffic,
             "avg_launch_ms": round(attn_ms, 5),
+            "timed": "HIP events on the launch stream around each verify_attn call: the attention kernel and "
+                     "its split-kv merge pass (about 14 us of the call), so the rate is slightly conservative",
             "algorithmic_flops": counts["flops"],
             "algorithmic_bytes": counts["attn_bytes"],
             "achieved_hbm_gbs": round(counts["attn_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
