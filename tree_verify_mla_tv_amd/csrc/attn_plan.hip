@@ -398,15 +398,13 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
 }  // namespace
 
 // Combine the pieces of split row blocks: w_s = l_s * exp(m_s - max m),
-// out = sum w_s o_s / sum w_s, lse = max m + log(sum w_s).
-// One thread per (merged row block, row, float4 column).
-__device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long idx) {
-  const int cpt = d_c / 4;
+// out = sum w_s o_s / sum w_s, lse = max m + log(sum w_s).  One thread per
+// (merged row block, row r within it, float4 column).  The pieces are read in
+// batches, all loads of a batch issued together, and the running max is
+// carried across batches by rescaling (one memory round trip per batch).
+__device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long mb, int r, int col4) {
   const int rpb = a.rows_per_block;
   const long long full_blocks = a.split_full > 1 ? static_cast<long long>(a.B) * a.full_rb : 0;
-  const int col4 = static_cast<int>(idx % cpt);
-  const int r = static_cast<int>((idx / cpt) % rpb);
-  const long long mb = idx / (static_cast<long long>(cpt) * rpb);
   int rb, n_split, R;
   long long slot0, row0;
   if (a.req) {
@@ -443,16 +441,8 @@ __device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long 
   }
   const int row = rb * rpb + r;
   if (row >= R) return;
-  // The pieces' loads are issued in batches with no branch between them, so a
-  // thread waits for one memory round trip per batch rather than per piece.
   constexpr int kBatch = 8;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (s0 + k < n_split) M = fmaxf(M, a.ws_m[(slot0 + s0 + k) * rpb + r]);
-  }
-  float W = 0.f;
+  float M = -INFINITY, W = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < n_split; s0 += kBatch) {
     float l[kBatch], m[kBatch];
@@ -465,16 +455,28 @@ __device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long 
       m[k] = in ? a.ws_m[sr] : 0.f;
       v[k] = in ? *reinterpret_cast<const float4*>(a.ws_o + sr * d_c + col4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    // pieces with no visible key (row sum 0) add nothing
+    float mb_max = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mb_max = l[k] > 0.f ? fmaxf(mb_max, m[k]) : mb_max;
+    if (mb_max == -INFINITY) continue;
+    const float Mn = fmaxf(M, mb_max);
+    const float sc = expf(M - Mn);  // 0 on the first batch with a visible key
+    W *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      // a piece with no visible key (row sum 0) adds nothing
-      const float w = l[k] > 0.f ? l[k] * expf(m[k] - M) : 0.f;
+      const float w = l[k] > 0.f ? l[k] * expf(m[k] - Mn) : 0.f;
       W += w;
       acc.x = fmaf(w, v[k].x, acc.x);
       acc.y = fmaf(w, v[k].y, acc.y);
       acc.z = fmaf(w, v[k].z, acc.z);
       acc.w = fmaf(w, v[k].w, acc.w);
     }
+    M = Mn;
   }
   const float inv = 1.f / W;
   const long long grow = row0 + row;
@@ -483,23 +485,53 @@ __device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long 
   if (col4 == 0 && a.lse) a.lse[grow] = M + logf(W);
 }
 
-// n_blocks: merged row blocks of a uniform batch; a ragged batch's count is
-// read from its records.  The grid strides over the work.
+// Threads cover the rows that exist: a uniform batch's merged full row blocks
+// (rows_per_block rows each), then its merged partial last blocks (R - (n_rb
+// - 1) rows_per_block rows each); a ragged batch's merged blocks (count from
+// its records) at rows_per_block rows each, rows past a request's end
+// returning at once.  The grid strides over them.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, long long n_blocks) {
-  if (a.req) n_blocks = req_totals(a.req, a.B)[kTotMerge];
-  const long long total = n_blocks * a.rows_per_block * (d_c / 4);
+  const int cpt = d_c / 4;
+  const int rpb = a.rows_per_block;
+  long long full_blocks, tail_rows;
+  if (a.req) {
+    full_blocks = req_totals(a.req, a.B)[kTotMerge];
+    tail_rows = rpb;
+  } else {
+    full_blocks = a.split_full > 1 ? static_cast<long long>(a.B) * a.full_rb : 0;
+    tail_rows = a.R - static_cast<long long>(a.n_rb - 1) * rpb;
+  }
+  const long long tail_blocks = a.req ? 0 : n_blocks - full_blocks;
+  const long long full_rows = full_blocks * rpb;
+  const long long total = (full_rows + tail_blocks * tail_rows) * cpt;
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
-  for (long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride)
-    merge_one(a, d_c, idx);
+  for (long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int col4 = static_cast<int>(idx % cpt);
+    const long long row_i = idx / cpt;
+    if (row_i < full_rows) {
+      merge_one(a, d_c, row_i / rpb, static_cast<int>(row_i % rpb), col4);
+    } else {
+      const long long t = row_i - full_rows;
+      merge_one(a, d_c, full_blocks + t / tail_rows, static_cast<int>(t % tail_rows), col4);
+    }
+  }
 }
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
   hipError_t e = plan.kernel == AttnKernel::kMfmaBf16 ? launch_attn_mfma_bf16(s, plan, a, stream)
                                                        : launch_attn_valu(s, plan, a, stream);
   if (e != hipSuccess || plan.merge_blocks == 0) return e;
-  const long long total = plan.merge_blocks * plan.rows_per_block * (s.d_c / 4);
-  long long grid = (total + 255) / 256;
-  if (a.req && grid > 8 * kNumCU) grid = 8 * kNumCU;  // ragged: an upper bound; the grid strides
+  long long rows;
+  if (a.req) {
+    rows = plan.merge_blocks * plan.rows_per_block;  // an upper bound; the grid strides
+  } else {
+    const long long full_blocks = plan.split_full > 1 ? static_cast<long long>(s.B) * plan.full_rb : 0;
+    const long long tail_rows = static_cast<long long>(s.q_len) * s.H - static_cast<long long>(plan.n_rb - 1) *
+                                                                          plan.rows_per_block;
+    rows = full_blocks * plan.rows_per_block + (plan.merge_blocks - full_blocks) * tail_rows;
+  }
+  long long grid = (rows * (s.d_c / 4) + 255) / 256;
+  if (a.req && grid > 8 * kNumCU) grid = 8 * kNumCU;
   attn_merge_kernel<<<dim3(static_cast<unsigned>(grid)), 256, 0, stream>>>(a, s.d_c, plan.merge_blocks);
   return hipGetLastError();
 }
