@@ -3,8 +3,8 @@
 max_abs = max |g - r| over every element.
 max_rel = max |g - r| / max(|r|, rms(r_row)), where r_row is the d_c-vector of
           the same (batch, node, head) output row.  The row floor keeps a
-          single near-zero reference element among ~10^7 from deciding the
-          verdict; the raw element-wise ratio is reported beside it.
+          single near-zero reference element among ~10^7 from deciding
+          pass or fail; the raw element-wise ratio is reported beside it.
 """
 from __future__ import annotations
 
