@@ -40,9 +40,9 @@ KERNELS = {
                  source=["tree_verify_mla_tv_amd/csrc/attn_mfma.hip", "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h",
                          "tree_verify_mla_tv_amd/csrc/tv_kernels.h"],
                  bound="mfma", peak="bf16", dtype="bf16"),
-    "f32": dict(name="attn_valu_kernel", source=["tree_verify_mla_tv_amd/csrc/attn_valu.hip",
-                                                "tree_verify_mla_tv_amd/csrc/tv_kernels.h"], bound="alu",
-                peak="f32_valu", dtype="f32"),
+    "f32": dict(name="attn_mfma_f32_kernel", source=["tree_verify_mla_tv_amd/csrc/attn_mfma_f32.hip",
+                                                    "tree_verify_mla_tv_amd/csrc/tv_kernels.h"], bound="mfma",
+                peak="f32_mfma", dtype="f32"),
 }
 
 
@@ -202,6 +202,36 @@ def reference_gemm(torch, n: int = 8192, reps: int = 10) -> dict:
     del a, b, c
     return {"what": f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) operands", "tflops": round(tf, 1),
             "frac_of_peak": round(tf / PEAKS_TFLOPS["bf16"], 4)}
+
+
+def fp32_configs(torch, tv, W) -> dict:
+    """The fp32-cache configurations: microseconds per verify_attn call
+    (inputs already rotated; the fp32 matrix-core kernel at d_c 512 / d_r 64,
+    the VALU kernel at 64 / 32), TFLOP/s against the fp32 peak (157.3 for
+    both) and GB/s, from the algorithmic counts."""
+    import numpy as np
+    dev = "cuda:0"
+    out = {}
+    for name, w in W.WORKLOADS.items():
+        if w.kv_dtype != "f32":
+            continue
+        inp = W.make_inputs(w)
+        t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+             for k in ("q_lat", "q_rope", "c_kv", "k_rope", "parent")}
+        o = torch.empty_like(t["q_lat"])
+        ws_n = tv.workspace_size(w.B, w.H, w.q_len, w.prefix_len, w.d_c, w.d_r, tv.TV_F32)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+        fn = lambda: tv.verify_attn(t["q_lat"], t["q_rope"], t["c_kv"], t["k_rope"], t["parent"], w.prefix_len,
+                                    w.sm_scale, out=o, workspace=ws)
+        for _ in range(20):
+            fn()
+        ms = _time_ms(torch, fn, 200)
+        c = algorithmic_counts(w, inp["parent"])
+        out[name] = {"us": round(ms * 1e3, 2), "tflops": round(c["flops"] / (ms * 1e-3) / 1e12, 2),
+                     "frac_of_fp32_peak": round(c["flops"] / (ms * 1e-3) / 1e12 / PEAKS_TFLOPS["f32_mfma"], 4),
+                     "kernel": "attn_mfma_f32_kernel" if (w.d_c, w.d_r) == (512, 64) else "attn_valu_kernel",
+                     "gbs": round(c["attn_bytes"] / (ms * 1e-3) / 1e9, 1)}
+    return out
 
 
 def verify_variants(torch, tv, W) -> dict:
@@ -387,6 +417,7 @@ def main() -> int:
     if args.next_rows and w.kv_dtype == "bf16":
         rec["next_rows"] = next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, args.cpu_sample > 0)
         rec["next_rows"]["verify_variants"] = verify_variants(torch, tv, W)
+        rec["next_rows"]["fp32_configs"] = fp32_configs(torch, tv, W)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -7,8 +7,11 @@ blocks within the launch bounds); a GPU test checks the device's records
 against it word for word."""
 
 TILE = 32
-SETUP = 10
-MIN_PIECE = 8
+# per-kernel planning costs (setup tiles, shortest piece in tiles, pieces the
+# merge pass combines per tile-step): the bf16 matrix-core and the VALU
+# kernels, and the fp32 matrix-core kernel
+COST_DEFAULT = (10, 8, 16)
+COST_F32 = (1, 1, 80)
 MAX_TAIL = 16
 N_BODY, N_TAIL = 4, 5
 N_CANDS = 1 + N_BODY * N_TAIL
@@ -28,14 +31,14 @@ def launch_bounds(B, H, max_q, rpb, target):
 NO_CUT = 1 << 30
 
 
-def caps(T0, c):
+def caps(T0, c, min_piece):
     if c == 0:
         return NO_CUT, NO_CUT
     i, j = divmod(c - 1, N_TAIL)
     num, den = (2, 3) if i == 0 else (1, 1 << (i - 1))
     body = min(T0, NO_CUT) * num // den
     tail = body >> j
-    return min(max(body, MIN_PIECE), NO_CUT), max(tail, MIN_PIECE)
+    return min(max(body, min_piece), NO_CUT), max(tail, min_piece)
 
 
 def cut(tiles, cap_b, cap_t):
@@ -58,7 +61,7 @@ def bucket_lo(k):
     return ((4 + (k & 3)) << (k >> 2)) >> 2
 
 
-def estimate(work, units, d_min, d_max, pieces, hist, M):
+def estimate(work, units, d_min, d_max, pieces, per_step, hist, M):
     e = float(work) / M + 0.5 * d_min
     e = max(e, float(d_max))
     if units > M:
@@ -68,7 +71,7 @@ def estimate(work, units, d_min, d_max, pieces, hist, M):
             if cum >= M + 1:
                 e = max(e, float(d_max + bucket_lo(k)))
                 break
-    return e + pieces / 16.0
+    return e + float(pieces) / per_step
 
 
 def req_len(prefix, q_len, b, H, max_q, kv_stride, rpb):
@@ -77,9 +80,10 @@ def req_len(prefix, q_len, b, H, max_q, kv_stride, rpb):
     return q, P, -(-(q * H) // rpb), -(-(P + q) // TILE)
 
 
-def plan(prefix, q_len, H, max_q, kv_stride, rpb, target):
+def plan(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=COST_DEFAULT):
     """The records: {"req": [dict per request], "cls_u0", "cls_id", "units",
     "merges", "choice"}."""
+    SETUP, min_piece, per_step = cost
     B = len(q_len)
     _, max_slots, _ = launch_bounds(B, H, max_q, rpb, target)
     rl = [req_len(prefix, q_len, b, H, max_q, kv_stride, rpb) for b in range(B)]
@@ -88,7 +92,7 @@ def plan(prefix, q_len, H, max_q, kv_stride, rpb, target):
     T0 = max(1, W0 // target)
     est = []
     for c in range(N_CANDS):
-        cb_, ct_ = caps(T0, c)
+        cb_, ct_ = caps(T0, c, min_piece)
         units = pieces = 0
         d_min, d_max = 1 << 31, 0
         hist = [0] * 64
@@ -112,12 +116,12 @@ def plan(prefix, q_len, H, max_q, kv_stride, rpb, target):
         if pieces > max_slots or units == 0:
             est.append(0.0 if c == 0 else -1.0)
         else:
-            est.append(estimate(Wt + SETUP * units, units, d_min, d_max, pieces, hist, target))
+            est.append(estimate(Wt + SETUP * units, units, d_min, d_max, pieces, per_step, hist, target))
     best = 0
     for c in range(1, N_CANDS):
         if est[c] >= 0.0 and est[c] < est[best]:
             best = c
-    cap_b, cap_t = caps(T0, best)
+    cap_b, cap_t = caps(T0, best, min_piece)
     reqs = []
     o_q = o_slot = o_merge = 0
     for q, P, nblk, tiles in rl:

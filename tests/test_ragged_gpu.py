@@ -167,7 +167,7 @@ def test_ragged_many_row_blocks_tail_pieces():
     _check(q_lens, prefixes, 64, 512, 64, "bf16")
 
 
-@pytest.mark.parametrize("which", ["bench_like", "uniform", "few_long", "many_short", "valu"])
+@pytest.mark.parametrize("which", ["bench_like", "uniform", "few_long", "many_short", "valu", "f32_mfma"])
 def test_ragged_records_match_plan_model(which):
     """The prep kernel's records (plan choice, class order, numbering) equal
     the host model's word for word, and the attention over them matches the
@@ -185,10 +185,14 @@ def test_ragged_records_match_plan_model(which):
     elif which == "many_short":
         q_lens = [int(x) for x in rng.integers(0, 20, 150)]
         prefixes = [int(x) for x in rng.integers(0, 600, 150)]
-    else:
+    elif which == "valu":
         dt, H, d_c, d_r = "f32", 4, 128, 32
         q_lens = [int(x) for x in rng.integers(1, 70, 12)]
         prefixes = [int(x) for x in rng.integers(0, 9000, 12)]
+    else:
+        dt, H, d_c, d_r = "f32", 8, 512, 64
+        q_lens = [int(x) for x in rng.integers(1, 70, 10)]
+        prefixes = [int(x) for x in rng.integers(0, 5000, 10)]
     max_q = max(q_lens)
     print(f"ragged records {which} B={len(q_lens)}", flush=True)
     q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs(q_lens, prefixes, H, d_c, d_r, dt, 5, seed=1)
@@ -202,8 +206,11 @@ def test_ragged_records_match_plan_model(which):
                                 torch.tensor(prefixes, dtype=torch.int32).cuda(),
                                 torch.tensor(q_lens, dtype=torch.int32).cuda(), max_q, sm, workspace=ws)
     torch.cuda.synchronize()
-    rpb, target = (128, 256) if dt == "bf16" and d_c == 512 and d_r == 64 else (16, 512)  # rows per workgroup
-    model = RP.records_words(RP.plan(prefixes, q_lens, H, max_q, S, rpb, target))
+    if d_c == 512 and d_r == 64:  # the matrix-core kernels: rows per workgroup, workgroups at once, costs
+        rpb, target, cost = (128, 256, RP.COST_DEFAULT) if dt == "bf16" else (64, 256, RP.COST_F32)
+    else:
+        rpb, target, cost = 16, 512, RP.COST_DEFAULT
+    model = RP.records_words(RP.plan(prefixes, q_lens, H, max_q, S, rpb, target, cost))
     got = ws[:4 * len(model)].view(torch.int32).cpu().numpy().tolist()
     assert got == model
     out = out.cpu().numpy()

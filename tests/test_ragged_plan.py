@@ -8,6 +8,7 @@ import pytest
 import ragged_plan_model as RP
 
 MFMA = dict(rpb=128, target=256)
+F32 = dict(rpb=64, target=256, cost=RP.COST_F32)
 VALU = dict(rpb=16, target=512)
 
 
@@ -30,8 +31,8 @@ def _merge_slots(rec, mb):
     return lo, r["n_blk"] - 1, [r["slot0"] + body * bs + s for s in range(r["t_split"])]
 
 
-def check(prefix, q_len, H, max_q, kv_stride, rpb, target):
-    rec = RP.plan(prefix, q_len, H, max_q, kv_stride, rpb, target)
+def check(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=RP.COST_DEFAULT):
+    rec = RP.plan(prefix, q_len, H, max_q, kv_stride, rpb, target, cost)
     bound_units, bound_slots, bound_merges = RP.launch_bounds(len(q_len), H, max_q, rpb, target)
     assert rec["units"] <= bound_units and rec["merges"] <= bound_merges
     covered = {}
@@ -87,7 +88,7 @@ def test_plan_covers_and_bounds(seed):
     rng = np.random.default_rng(seed)
     for q_len, prefix, H, max_q in _families(rng):
         kv_stride = max(p + q for p, q in zip(prefix, q_len)) + 3
-        for kern in (MFMA, VALU):
+        for kern in (MFMA, F32, VALU):
             check(prefix, q_len, H, max_q, kv_stride, **kern)
 
 
@@ -99,6 +100,7 @@ def test_plan_edge_cases():
     check([0] * 5, [0] * 5, 4, 8, 64, **VALU)
     check([200000], [64], 128, 64, 200064, **MFMA)   # one request, many row blocks, long prefix
     check([300, 40000], [256, 1], 2, 256, 40256, **VALU)
+    check([300, 40000, 0], [256, 1, 7], 2, 256, 40256, **F32)
 
 
 def test_plan_unsorted_large_batch():

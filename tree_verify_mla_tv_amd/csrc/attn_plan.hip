@@ -15,14 +15,19 @@ namespace tv {
 namespace {
 constexpr int kNumCU = 256;          // MI355X; fixed so plans depend on shapes only
 constexpr int kMinKeysPerSplit = 256;
+// The fp32 matrix-core kernel's tile-step is ~6x the bf16 kernel's (the same
+// flops at a sixteenth of the rate, over half the rows), so its set-up is worth
+// about one tile and pieces may be as short as one tile.
+constexpr int kF32SetupTiles = 1;
+constexpr int kF32MinKeysPerSplit = kF32Keys;
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
 
 // Cut kv_len rows into at most `want` ranges of a whole number of tiles.
-void cut(int kv_len, int want, int tile, int& n, int& chunk) {
-  const int max_split = kv_len / kMinKeysPerSplit > 1 ? kv_len / kMinKeysPerSplit : 1;
+void cut(int kv_len, int want, int tile, int& n, int& chunk, int min_keys = kMinKeysPerSplit) {
+  const int max_split = kv_len / min_keys > 1 ? kv_len / min_keys : 1;
   n = want < 1 ? 1 : (want > max_split ? max_split : want);
   chunk = ceil_div(kv_len, n);
   chunk = ceil_div(chunk, tile) * tile;
@@ -35,13 +40,14 @@ void cut(int kv_len, int want, int tile, int& n, int& chunk) {
 // in tile-steps); ties go to fewer splits (less merging).  Rounding the count
 // up instead (blocks x splits just above slots) would add a nearly empty
 // second round.
-void cut_for_blocks(int kv_len, long long blocks, long long slots, int tile, int setup_tiles, int& n, int& chunk) {
-  const int max_split = kv_len / kMinKeysPerSplit > 1 ? kv_len / kMinKeysPerSplit : 1;
+void cut_for_blocks(int kv_len, long long blocks, long long slots, int tile, int setup_tiles, int& n, int& chunk,
+                    int min_keys = kMinKeysPerSplit) {
+  const int max_split = kv_len / min_keys > 1 ? kv_len / min_keys : 1;
   long long best_cost = -1;
   int best = 1;
   for (int want = 1; want <= max_split; ++want) {
     int sn, sc;
-    cut(kv_len, want, tile, sn, sc);
+    cut(kv_len, want, tile, sn, sc, min_keys);
     if (sn != want) continue;  // an equivalent cut was already counted
     const long long rounds = (blocks * sn + slots - 1) / slots;
     const long long cost = rounds * (sc / tile + setup_tiles);
@@ -50,29 +56,31 @@ void cut_for_blocks(int kv_len, long long blocks, long long slots, int tile, int
       best = sn;
     }
   }
-  cut(kv_len, best, tile, n, chunk);
+  cut(kv_len, best, tile, n, chunk, min_keys);
 }
 }  // namespace
 
 AttnPlan plan_attention(const AttnShape& s) {
   AttnPlan p{};
   const bool mfma = s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
-  p.kernel = mfma ? AttnKernel::kMfmaBf16 : AttnKernel::kValu;
-  p.rows_per_block = mfma ? kMfmaRows : kValuRows;
+  const bool f32 = !s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
+  p.kernel = mfma ? AttnKernel::kMfmaBf16 : f32 ? AttnKernel::kMfmaF32 : AttnKernel::kValu;
+  p.rows_per_block = mfma ? kMfmaRows : f32 ? kF32Rows : kValuRows;
   p.keys_per_tile = mfma ? kMfmaKeys : kValuKeys;
   const int R = s.q_len * s.H;
   p.n_rb = ceil_div(R, p.rows_per_block);
   const bool has_tail = (R % p.rows_per_block) != 0;
   p.full_rb = has_tail ? p.n_rb - 1 : p.n_rb;
-  // Workgroups resident per CU: the MFMA kernel takes a whole CU; the VALU one
-  // about one (its LDS is ~114 KB at d_c = 512), so aim at two rounds for it.
-  const long long target = mfma ? kNumCU : 2 * kNumCU;
+  // Workgroups resident per CU: a matrix-core kernel takes a whole CU; the VALU
+  // one about one, so aim at two rounds for it.
+  const long long target = mfma || f32 ? kNumCU : 2 * kNumCU;
 
   const long long blocks = static_cast<long long>(s.B) * p.n_rb;
   if (blocks < target) {
     // Too few row blocks: cut every block's kv range.  A unit's set-up (tree
     // masks, queries, first tile, output) costs about ten tile-steps.
-    cut_for_blocks(s.kv_len, blocks, target, p.keys_per_tile, 10, p.split_full, p.chunk_full);
+    cut_for_blocks(s.kv_len, blocks, target, p.keys_per_tile, f32 ? kF32SetupTiles : 10, p.split_full, p.chunk_full,
+                   f32 ? kF32MinKeysPerSplit : kMinKeysPerSplit);
     p.split_tail = p.split_full;
     p.chunk_tail = p.chunk_full;
   } else {
@@ -85,7 +93,8 @@ AttnPlan plan_attention(const AttnShape& s) {
       long long free_slots = target - full_units % target;
       const long long tails = s.B;
       if (free_slots < tails) free_slots += target;
-      cut(s.kv_len, static_cast<int>(free_slots / tails), p.keys_per_tile, p.split_tail, p.chunk_tail);
+      cut(s.kv_len, static_cast<int>(free_slots / tails), p.keys_per_tile, p.split_tail, p.chunk_tail,
+          f32 ? kF32MinKeysPerSplit : kMinKeysPerSplit);
     }
   }
   if (p.full_rb == 0) {  // only a partial block per tree
@@ -118,14 +127,15 @@ AttnPlan plan_attention(const AttnShape& s) {
 AttnPlan plan_attention_ragged(const AttnShape& s) {
   AttnPlan p{};
   const bool mfma = s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
-  p.kernel = mfma ? AttnKernel::kMfmaBf16 : AttnKernel::kValu;
-  p.rows_per_block = mfma ? kMfmaRows : kValuRows;
+  const bool f32 = !s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
+  p.kernel = mfma ? AttnKernel::kMfmaBf16 : f32 ? AttnKernel::kMfmaF32 : AttnKernel::kValu;
+  p.rows_per_block = mfma ? kMfmaRows : f32 ? kF32Rows : kValuRows;
   p.keys_per_tile = mfma ? kMfmaKeys : kValuKeys;
   p.n_rb = ceil_div(static_cast<long long>(s.q_len) * s.H, p.rows_per_block);
   p.full_rb = p.n_rb;
   p.split_full = p.split_tail = 1;
   p.chunk_full = p.chunk_tail = s.kv_len;
-  p.target = mfma ? kNumCU : 2 * kNumCU;
+  p.target = mfma || f32 ? kNumCU : 2 * kNumCU;
   const long long blocks = static_cast<long long>(s.B) * p.n_rb;
   const long long cap = static_cast<long long>(s.B) * kMaxTailSplit;
   p.n_slots = 2 * p.target > cap ? 2 * p.target : cap;
@@ -141,7 +151,8 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
 
 namespace {
 
-static_assert(kMfmaKeys == kPlanTile && kValuKeys == kPlanTile, "plans count tiles of 32 keys for both kernels");
+static_assert(kMfmaKeys == kPlanTile && kValuKeys == kPlanTile && kF32Keys == kPlanTile,
+              "plans count tiles of 32 keys for every kernel");
 
 // Lengths of request b clamped into the bounds (q_len to [0, max_q], prefix
 // to [0, kv_stride - q_len]); its row blocks and tiles.
@@ -207,7 +218,8 @@ __device__ int block_scan(int v, int* s_wave, int* total) {
 __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t* __restrict__ prefix_len,
                                                                    const int32_t* __restrict__ q_len, int B, int H,
                                                                    int max_q, int kv_stride, int rpb, int target,
-                                                                   int max_slots, int32_t* __restrict__ rq) {
+                                                                   int max_slots, PlanCost cost,
+                                                                   int32_t* __restrict__ rq) {
   __shared__ long long s_part[kPrepThreads / 64];
   __shared__ unsigned long long s_units[kPlanCands], s_pieces[kPlanCands];
   __shared__ int s_dmin[kPlanCands], s_dmax[kPlanCands];
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   long long w0 = 0, wt = 0;
   for (int b = b0; b < b1; ++b) {
     const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
-    w0 += static_cast<long long>(r.nblk) * (r.tiles + kPlanSetupTiles);
+    w0 += static_cast<long long>(r.nblk) * (r.tiles + cost.setup);
     wt += static_cast<long long>(r.nblk) * r.tiles;
   }
   const long long T0 = max(1ll, block_sum(w0, s_part) / target);
@@ -235,7 +247,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
     s_units[t] = s_pieces[t] = 0;
     s_dmin[t] = INT_MAX;
     s_dmax[t] = 0;
-    plan_caps(T0, t, s_capb[t], s_capt[t]);
+    plan_caps(T0, t, cost.min_piece, s_capb[t], s_capt[t]);
   }
   __syncthreads();
   // One (request, candidate) pair per thread at a time.
@@ -251,23 +263,23 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
         (k.n_body > 1 ? static_cast<unsigned long long>(nb) * k.n_body : 0ull) + (k.n_tail > 1 ? k.n_tail : 0);
     atomicAdd(&s_units[c], units);
     if (pieces) atomicAdd(&s_pieces[c], pieces);
-    atomicMin(&s_dmin[c], min(nb ? last_b : INT_MAX, last_t) + kPlanSetupTiles);
-    atomicMax(&s_dmax[c], max(nb ? k.c_body : 0, k.c_tail) + kPlanSetupTiles);
+    atomicMin(&s_dmin[c], min(nb ? last_b : INT_MAX, last_t) + cost.setup);
+    atomicMax(&s_dmax[c], max(nb ? k.c_body : 0, k.c_tail) + cost.setup);
     // (counts of candidates past the slot budget may wrap; those are never read)
     if (nb) {
-      if (k.n_body > 1) atomicAdd(&s_hist[c][plan_bucket(k.c_body + kPlanSetupTiles)], nb * (k.n_body - 1));
-      atomicAdd(&s_hist[c][plan_bucket(last_b + kPlanSetupTiles)], nb);
+      if (k.n_body > 1) atomicAdd(&s_hist[c][plan_bucket(k.c_body + cost.setup)], nb * (k.n_body - 1));
+      atomicAdd(&s_hist[c][plan_bucket(last_b + cost.setup)], nb);
     }
-    if (k.n_tail > 1) atomicAdd(&s_hist[c][plan_bucket(k.c_tail + kPlanSetupTiles)], k.n_tail - 1);
-    atomicAdd(&s_hist[c][plan_bucket(last_t + kPlanSetupTiles)], 1);
+    if (k.n_tail > 1) atomicAdd(&s_hist[c][plan_bucket(k.c_tail + cost.setup)], k.n_tail - 1);
+    atomicAdd(&s_hist[c][plan_bucket(last_t + cost.setup)], 1);
   }
   __syncthreads();
   if (t < kPlanCands) {
     const long long units = static_cast<long long>(s_units[t]);
     s_est[t] = static_cast<long long>(s_pieces[t]) > max_slots || units == 0
                    ? (t == 0 ? 0.0 : -1.0)
-                   : plan_estimate(Wt + kPlanSetupTiles * units, units, s_dmin[t], s_dmax[t],
-                                   static_cast<long long>(s_pieces[t]), s_hist[t], target);
+                   : plan_estimate(Wt + cost.setup * units, units, s_dmin[t], s_dmax[t],
+                                   static_cast<long long>(s_pieces[t]), cost.pieces_per_step, s_hist[t], target);
   }
   __syncthreads();
   if (t == 0) {
@@ -518,7 +530,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, lo
 }
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  hipError_t e = plan.kernel == AttnKernel::kMfmaBf16 ? launch_attn_mfma_bf16(s, plan, a, stream)
+  hipError_t e = plan.kernel == AttnKernel::kMfmaBf16  ? launch_attn_mfma_bf16(s, plan, a, stream)
+                 : plan.kernel == AttnKernel::kMfmaF32 ? launch_attn_mfma_f32(s, plan, a, stream)
                                                        : launch_attn_valu(s, plan, a, stream);
   if (e != hipSuccess || plan.merge_blocks == 0) return e;
   long long rows;
@@ -540,7 +553,10 @@ hipError_t launch_ragged_prep(const AttnShape& s, const AttnPlan& plan, const At
                               const int32_t* q_len, hipStream_t stream) {
   ragged_prep_kernel<<<dim3(1), kPrepThreads, 0, stream>>>(prefix_len, q_len, s.B, s.H, s.q_len, s.kv_len,
                                                            plan.rows_per_block, static_cast<int>(plan.target),
-                                                           static_cast<int>(plan.n_slots), const_cast<int32_t*>(a.req));
+                                                           static_cast<int>(plan.n_slots),
+                                                           plan.kernel == AttnKernel::kMfmaF32 ? kPlanCostF32
+                                                                                               : kPlanCostDefault,
+                                                           const_cast<int32_t*>(a.req));
   return hipGetLastError();
 }
 

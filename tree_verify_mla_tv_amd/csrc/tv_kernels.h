@@ -35,15 +35,20 @@ hipError_t launch_tree_rope_ragged(float* q_rope, void* k_rope, bool bf16, const
 // ---------------------------------------------------------------------------
 // Attention
 // ---------------------------------------------------------------------------
-enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1 };
+enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1, kMfmaF32 = 2 };
 
-// Workgroup geometry of the two kernel families.
+// Workgroup geometry of the three kernels: the bf16-cache matrix-core kernel
+// (d_c 512, d_r 64), the fp32-cache matrix-core kernel (the same dims) and the
+// vector-ALU kernel (every other supported shape).
 constexpr int kValuRows = 16;     // query rows per workgroup
 constexpr int kValuKeys = 32;     // kv rows per LDS tile
 constexpr int kValuThreads = 256;
 constexpr int kMfmaRows = 128;    // 4 waves x 32 query rows
 constexpr int kMfmaKeys = 32;
 constexpr int kMfmaThreads = 256;
+constexpr int kF32Rows = 64;      // 4 waves x 16 query rows
+constexpr int kF32Keys = 32;
+constexpr int kF32Threads = 256;
 // Tiles of a unit that hold tree keys or the unit's range end: at most
 // q_len / 32 + 2.
 constexpr int kMaxBoundaryTiles = kMaxQ / kMfmaKeys + 2;
@@ -134,26 +139,34 @@ __host__ __device__ inline const int32_t* req_totals(const int32_t* rq, int B) {
 }
 __host__ __device__ inline size_t req_words(int B) { return static_cast<size_t>(B) * (kReqFields + 4) + kReqTotals; }
 
-// Planning of a ragged batch, in tiles of 32 keys (both kernels' tile).  A
-// unit costs its tiles plus kPlanSetupTiles (tree masks, queries, first tile,
-// output).  Candidate plans cap the pieces of the row blocks before the last
-// at cap_body tiles and those of the last block at cap_tail (at most
-// kMaxTailSplit pieces, but never fewer than the other blocks get): the last
-// blocks' shorter pieces fill the gaps the longer units leave.  Candidate 0
-// cuts nothing; the others take cap_body = T0 x {2/3, 1, 1/2, 1/4} and
-// cap_tail = cap_body / {1, 2, 4, 8, 16}, T0 = the whole batch's cost per
-// concurrent workgroup.
+// Planning of a ragged batch, in tiles of 32 keys (every kernel's tile).  A
+// unit costs its tiles plus a set-up (tree masks, queries, first tile,
+// output) of PlanCost::setup tiles.  Candidate plans cap the pieces of the
+// row blocks before the last at cap_body tiles and those of the last block at
+// cap_tail (at most kMaxTailSplit pieces, but never fewer than the other
+// blocks get): the last blocks' shorter pieces fill the gaps the longer units
+// leave.  Candidate 0 cuts nothing; the others take cap_body = T0 x {2/3, 1,
+// 1/2, 1/4} and cap_tail = cap_body / {1, 2, 4, 8, 16} (at least
+// PlanCost::min_piece tiles), T0 = the whole batch's cost per concurrent
+// workgroup.
 constexpr int kPlanTile = 32;
-constexpr int kPlanSetupTiles = 10;
-constexpr int kMinPieceTiles = 8;
 constexpr int kMaxTailSplit = 16;
+struct PlanCost {
+  int setup;            // tiles
+  int min_piece;        // tiles
+  int pieces_per_step;  // split pieces the merge pass combines per tile-step of the whole GPU
+};
+// The bf16 matrix-core and the VALU kernels: a unit's set-up is ~10 of their
+// tile-steps; the fp32 matrix-core kernel's tile-step is ~5x longer.
+constexpr PlanCost kPlanCostDefault{10, 8, 16};
+constexpr PlanCost kPlanCostF32{1, 1, 80};
 constexpr int kPlanBody = 4, kPlanTail = 5;
 constexpr int kPlanCands = 1 + kPlanBody * kPlanTail;
 
 // Caps of candidate c given T0 (tiles); at most kPlanNoCut, which no request
 // reaches (tiles < 2^26), so larger caps cut nothing either.
 constexpr int kPlanNoCut = 1 << 30;
-__host__ __device__ inline void plan_caps(long long T0, int c, int& cap_body, int& cap_tail) {
+__host__ __device__ inline void plan_caps(long long T0, int c, int min_piece, int& cap_body, int& cap_tail) {
   if (c == 0) {
     cap_body = cap_tail = kPlanNoCut;
     return;
@@ -163,8 +176,8 @@ __host__ __device__ inline void plan_caps(long long T0, int c, int& cap_body, in
   const long long den = i == 0 ? 3 : (1 << (i - 1));
   long long body = (T0 < kPlanNoCut ? T0 : kPlanNoCut) * num / den;
   long long tail = body >> j;
-  body = body < kMinPieceTiles ? kMinPieceTiles : (body > kPlanNoCut ? kPlanNoCut : body);
-  tail = tail < kMinPieceTiles ? kMinPieceTiles : tail;
+  body = body < min_piece ? min_piece : (body > kPlanNoCut ? kPlanNoCut : body);
+  tail = tail < min_piece ? min_piece : tail;
   cap_body = static_cast<int>(body);
   cap_tail = static_cast<int>(tail);
 }
@@ -200,10 +213,11 @@ __host__ __device__ inline long long plan_bucket_lo(int k) { return (static_cast
 // Estimated span of a candidate, in tile-steps: the work per workgroup plus
 // half the shortest unit (the last units fill gaps), at least the longest
 // unit, and with more units than workgroups at least the longest unit plus the
-// (M+1)-th longest (some workgroup runs two); plus the merge pass, about one
-// tile-step of the whole GPU per 16 pieces.
+// (M+1)-th longest (some workgroup runs two); plus the merge pass, one
+// tile-step of the whole GPU per pieces_per_step pieces.
 __host__ __device__ inline double plan_estimate(long long work, long long units, long long d_min, long long d_max,
-                                                long long pieces, const int* hist, long long M) {
+                                                long long pieces, int pieces_per_step, const int* hist,
+                                                long long M) {
   double e = static_cast<double>(work) / M + 0.5 * d_min;
   e = e > d_max ? e : static_cast<double>(d_max);
   if (units > M) {
@@ -217,7 +231,7 @@ __host__ __device__ inline double plan_estimate(long long work, long long units,
       }
     }
   }
-  return e + pieces / 16.0;
+  return e + static_cast<double>(pieces) / pieces_per_step;
 }
 
 // The work of one unit (one workgroup), with the shape of its request.
@@ -396,6 +410,7 @@ hipError_t launch_tree_build(const float* logp, const int32_t* cand_tok, const i
 // Kernel launchers (one per kernel family).
 hipError_t launch_attn_valu(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_mfma_bf16(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_mfma_f32(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 
 // Ancestor bit masks of one tree: bit m % 64 of word s_anc[i * kAncWords +
 // m / 64] is set iff node m is node i or one of its ancestors (words past the
