@@ -19,7 +19,7 @@ constexpr int kMinKeysPerSplit = 256;
 // flops at a sixteenth of the rate, over half the rows), so its set-up is worth
 // about one tile and pieces may be as short as one tile.
 constexpr int kF32SetupTiles = 1;
-constexpr int kF32MinKeysPerSplit = kF32Keys;
+constexpr int kF32MinKeysPerSplit = kF32Keys / 2;  // pieces still round up to whole tiles
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
