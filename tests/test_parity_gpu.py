@@ -279,3 +279,32 @@ def test_bf16_late_large_scores_resweep():
                               cuda_cache(k_rope, "bf16"), torch.from_numpy(parent).cuda(), P, sm, return_lse=True)
     torch.cuda.synchronize()
     check_out("late-large-scores", "B1 H4 q3 P300", out, lse, ref_out, ref_lse, "bf16")
+
+
+@pytest.mark.parametrize("q", [1, 3])
+def test_fp32_tree_key_at_every_tile_position(q):
+    """Prefix lengths 28 .. 71 put the first tree key at every position of a
+    key tile, in units of one, two and three tiles, with and without kv
+    pieces (B = 1 splits the kv range, B = 256 does not).  The fp32
+    matrix-core kernel once dropped a visible tree key held in score
+    register 0 of a later tile; every case here is checked against the
+    oracle."""
+    d_c, d_r = 512, 64
+    for B, H in ((1, 16), (256, 4)):
+        rng = np.random.default_rng(B + q)
+        ql = rng.standard_normal((B, q, H, d_c), dtype=np.float32)
+        qr = rng.standard_normal((B, q, H, d_r), dtype=np.float32)
+        ck_all = rng.standard_normal((B, 71 + q, d_c), dtype=np.float32)
+        kr_all = rng.standard_normal((B, 71 + q, d_r), dtype=np.float32)
+        par = np.stack([W.tree_chain(q) for _ in range(B)]).astype(np.int32)
+        args = (cuda_f32(ql), cuda_f32(qr))
+        rows = [0, B - 1]
+        for P in range(28, 72):
+            ck = np.ascontiguousarray(ck_all[:, :P + q])
+            kr = np.ascontiguousarray(kr_all[:, :P + q])
+            out = tv.verify_attn(*args, cuda_f32(ck), cuda_f32(kr), torch.from_numpy(par).cuda(), P,
+                                 0.04).cpu().numpy()
+            ref, _ = O.verify_attn(ql[rows].astype(np.float64), qr[rows].astype(np.float64),
+                                   ck[rows].astype(np.float64), kr[rows].astype(np.float64), par[rows], P, 0.04)
+            e = errors(out[rows], ref)
+            assert e["max_abs"] <= 1e-5 and e["max_rel"] <= 1e-2, (B, P, q, e)
