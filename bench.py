@@ -305,6 +305,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the reference launch that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
+    ap.add_argument("--fp32-configs", action="store_true",
+                    help="only time the fp32-cache configurations (next_rows.fp32_configs), print them as one "
+                         "JSON line and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -322,6 +325,10 @@ def main() -> int:
 
     from tree_verify_mla_tv_amd import tv
     from tree_verify_mla_tv_amd import workloads as W
+
+    if args.fp32_configs:
+        print(json.dumps({"fp32_configs": fp32_configs(torch, tv, W)}), flush=True)
+        return 0
 
     w = W.WORKLOADS[args.workload or W.SERVING]
     tv.load()
