@@ -118,6 +118,12 @@ tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t 
  *   kv_dtype TV_F32 or TV_BF16.  1 <= q_len <= TV_MAX_Q_LEN.  One tree's
  *   latent rows (kv_len * d_c elements of kv_dtype) must stay below 2^31
  *   bytes (TV_ERR_UNSUPPORTED otherwise).
+ *   Arithmetic: with a bf16 cache at (512, 64) both contractions run on bf16
+ *   matrix cores (the scaled queries and the softmax weights rounded to bf16,
+ *   fp32 accumulation and row sums); with an fp32 cache at (512, 64) on fp32
+ *   matrix cores; other shapes on the fp32 vector ALU.  The sums run in a
+ *   different order than the plain definition; the results agree with it to
+ *   fp32 (or, for the bf16 path, bf16-operand) rounding.
  *   workspace: caller-owned device scratch of at least
  *   tv_verify_attn_workspace_size(...) bytes (NULL allowed when that is 0).
  *   out must not overlap any input.
