@@ -143,6 +143,12 @@ EDGE = [
     (1, 3, 64, 1, 512, 64, "bf16", "rrt"),        # largest tree, 1-row prefix
     (2, 64, 9, 4097, 512, 64, "bf16", "branch4"), # few blocks: every block split
     (5, 32, 17, 333, 512, 64, "bf16", "wide"),    # ragged rows and kv tail
+    # fp32 cache, d_c = 512, d_r = 64: the fp32 matrix-core kernel
+    (3, 1, 256, 0, 512, 64, "f32", "rrt"),        # tree keys only, 4-word masks, 4 row blocks
+    (1, 1, 1, 0, 512, 64, "f32", "chain"),        # one row, one key
+    (5, 3, 17, 64, 512, 64, "f32", "wide"),       # prefix of exactly two tiles, partial row block
+    (2, 64, 33, 700, 512, 64, "f32", "branch4"),  # full 64-row blocks, kv pieces
+    (4, 16, 8, 0, 512, 64, "f32", "chain"),       # R = 128: two full blocks, causal prefill
 ]
 
 
