@@ -23,7 +23,7 @@ FIELDS = ("q_start", "q_len", "prefix", "n_blk", "b_split", "b_chunk", "t_split"
 def launch_bounds(B, H, max_q, rpb, target):
     """(units, slots, merged blocks) the host sizes the launch for."""
     n_rb = -(-(max_q * H) // rpb)
-    slots = max(2 * target, MAX_TAIL * B)
+    slots = max(2 * target, min(MAX_TAIL * B, 4 * target))
     blocks = B * n_rb
     return blocks + slots, slots, min(blocks, slots // 2)
 

@@ -121,9 +121,10 @@ AttnPlan plan_attention(const AttnShape& s) {
 // Ragged batch: launch sizes from the bounds (B requests of at most max_q_len
 // nodes over at most kv_stride keys); the prep kernel makes the plan from the
 // device lengths.  Partial-result slots are capped at max(2 target,
-// kMaxTailSplit B) (a candidate plan needing more is not taken; cutting
-// nothing needs none).  Every unit is a row block whole or a split piece, so
-// units <= B n_rb + slots; merged blocks <= min(B n_rb, slots / 2).
+// min(kMaxTailSplit B, 4 target)) (a candidate plan needing more is not
+// taken; cutting nothing needs none; more than four rounds of pieces never
+// pays).  Every unit is a row block whole or a split piece, so units <= B n_rb
+// + slots; merged blocks <= min(B n_rb, slots / 2).
 AttnPlan plan_attention_ragged(const AttnShape& s) {
   AttnPlan p{};
   const bool mfma = s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
@@ -137,7 +138,8 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
   p.chunk_full = p.chunk_tail = s.kv_len;
   p.target = mfma || f32 ? kNumCU : 2 * kNumCU;
   const long long blocks = static_cast<long long>(s.B) * p.n_rb;
-  const long long cap = static_cast<long long>(s.B) * kMaxTailSplit;
+  long long cap = static_cast<long long>(s.B) * kMaxTailSplit;
+  cap = cap < 4 * p.target ? cap : 4 * p.target;
   p.n_slots = 2 * p.target > cap ? 2 * p.target : cap;
   p.units = blocks + p.n_slots;
   p.merge_blocks = blocks < p.n_slots / 2 ? blocks : p.n_slots / 2;
