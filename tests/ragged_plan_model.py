@@ -150,7 +150,27 @@ def plan(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=COST_DEFAULT):
     for i in ids:
         u0.append(u)
         u += cls(i)[0]
-    return dict(req=reqs, cls_u0=u0, cls_id=ids, units=u, merges=o_merge, choice=best, max_slots=max_slots)
+    return dict(req=reqs, cls_u0=u0, cls_id=ids, units=u, merges=o_merge, choice=best, max_slots=max_slots, H=H,
+                rpb=rpb)
+
+
+def merge_table(rec):
+    """Per merged row block, in merged-block order: (first slot, pieces, first
+    output row, rows that exist)."""
+    H, rpb = rec["H"], rec["rpb"]
+    tab = []
+    for r in rec["req"]:
+        if r["n_blk"] == 0:
+            continue
+        body = r["n_blk"] - 1 if r["b_split"] > 1 else 0
+        for m in range(body):
+            tab.append((r["slot0"] + m * r["b_split"], r["b_split"], r["q_start"] * H + m * rpb, rpb))
+        if r["t_split"] > 1:
+            rb = r["n_blk"] - 1
+            tab.append((r["slot0"] + body * r["b_split"], r["t_split"], r["q_start"] * H + rb * rpb,
+                        r["q_len"] * H - rb * rpb))
+    assert len(tab) == rec["merges"]
+    return tab
 
 
 def decode(rec, x, H):
@@ -185,8 +205,14 @@ def decode(rec, x, H):
 
 
 def records_words(rec):
-    """The records as the device lays them out (int32 words)."""
+    """The records and the merge table as the device lays them out (int32
+    words; the table starts at the next multiple of four words, the gap
+    unwritten and read as zero from a zeroed workspace)."""
     words = []
     for r in rec["req"]:
         words += [r[f] for f in FIELDS]
-    return words + rec["cls_u0"] + rec["cls_id"] + [rec["units"], rec["merges"], rec["choice"]]
+    words += rec["cls_u0"] + rec["cls_id"] + [rec["units"], rec["merges"], rec["choice"]]
+    words += [0] * (-len(words) % 4)
+    for e in merge_table(rec):
+        words += list(e)
+    return words

@@ -13,22 +13,10 @@ VALU = dict(rpb=16, target=512)
 
 
 def _merge_slots(rec, mb):
-    """Row block and slots of merged block mb, as attn_merge_kernel reads them."""
-    reqs = rec["req"]
-    lo, hi = 0, len(reqs) - 1
-    while lo < hi:
-        mid = (lo + hi + 1) >> 1
-        if reqs[mid]["merge0"] <= mb:
-            lo = mid
-        else:
-            hi = mid - 1
-    r = reqs[lo]
-    m = mb - r["merge0"]
-    bs = r["b_split"]
-    body = r["n_blk"] - 1 if bs > 1 else 0
-    if m < body:
-        return lo, m, [r["slot0"] + m * bs + s for s in range(bs)]
-    return lo, r["n_blk"] - 1, [r["slot0"] + body * bs + s for s in range(r["t_split"])]
+    """Rows and slots of merged block mb, as attn_merge_ragged_kernel reads
+    them from the merge table."""
+    slot0, n, row0, rows = RP.merge_table(rec)[mb]
+    return row0, rows, [slot0 + s for s in range(n)]
 
 
 def check(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=RP.COST_DEFAULT):
@@ -63,9 +51,14 @@ def check(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=RP.COST_DEFAULT)
             if len(pieces) == 1:
                 assert all(v[:2] != (b, rb) for v in slots.values())
     # merged blocks: exactly the split row blocks, each reading its own slots
+    # and writing its own rows
     seen = set()
     for mb in range(rec["merges"]):
-        b, rb, sl = _merge_slots(rec, mb)
+        row0, rows, sl = _merge_slots(rec, mb)
+        b = max(i for i, r in enumerate(rec["req"]) if r["n_blk"] and r["q_start"] * H <= row0)
+        r = rec["req"][b]
+        rb, off = divmod(row0 - r["q_start"] * H, rpb)
+        assert off == 0 and rb < r["n_blk"] and rows == min(rpb, r["q_len"] * H - rb * rpb), (mb, b, rb)
         assert (b, rb) not in seen and len(sl) > 1
         seen.add((b, rb))
         assert sorted(sl) == sorted(s for s, v in slots.items() if v[:2] == (b, rb)), (b, rb)

@@ -143,7 +143,8 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
   p.n_slots = 2 * p.target > cap ? 2 * p.target : cap;
   p.units = blocks + p.n_slots;
   p.merge_blocks = blocks < p.n_slots / 2 ? blocks : p.n_slots / 2;
-  const size_t rec = align256(req_words(s.B) * sizeof(int32_t));
+  const size_t rec = align256((merge_table_word0(s.B) + static_cast<size_t>(p.merge_blocks) * kMtFields) *
+                              sizeof(int32_t));
   p.ws_o_off = rec;
   p.ws_m_off = rec + align256(static_cast<size_t>(p.n_slots) * p.rows_per_block * s.d_c * sizeof(float));
   p.ws_l_off = p.ws_m_off + align256(static_cast<size_t>(p.n_slots) * p.rows_per_block * sizeof(float));
@@ -220,7 +221,7 @@ __device__ int block_scan(int v, int* s_wave, int* total) {
 __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t* __restrict__ prefix_len,
                                                                    const int32_t* __restrict__ q_len, int B, int H,
                                                                    int max_q, int kv_stride, int rpb, int target,
-                                                                   int max_slots, PlanCost cost,
+                                                                   int max_slots, int max_merges, PlanCost cost,
                                                                    int32_t* __restrict__ rq) {
   __shared__ long long s_part[kPrepThreads / 64];
   __shared__ unsigned long long s_units[kPlanCands], s_pieces[kPlanCands];
@@ -322,6 +323,14 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
     o[kReqTChunk] = k.c_tail * kPlanTile;
     o[kReqSlot0] = o_slot;
     o[kReqMerge0] = o_merge;
+    // Merge table: the blocks before the last (if cut), then the last (if cut).
+    int4* mt = reinterpret_cast<int4*>(rq + merge_table_word0(B));
+    const int body = k.n_body > 1 && r.nblk > 1 ? r.nblk - 1 : 0;
+    for (int m = 0; m < body && o_merge + m < max_merges; ++m)
+      mt[o_merge + m] = make_int4(o_slot + m * k.n_body, k.n_body, o_q * H + m * rpb, rpb);
+    if (r.nblk > 0 && k.n_tail > 1 && o_merge + body < max_merges)
+      mt[o_merge + body] = make_int4(o_slot + body * k.n_body, k.n_tail, o_q * H + (r.nblk - 1) * rpb,
+                                     r.q * H - (r.nblk - 1) * rpb);
     if (r.nblk > 0) {
       o_q += r.q;
       o_slot += (k.n_body > 1 ? (r.nblk - 1) * k.n_body : 0) + (k.n_tail > 1 ? k.n_tail : 0);
@@ -416,63 +425,64 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
 // (merged row block, row r within it, float4 column).  The pieces are read in
 // batches, all loads of a batch issued together, and the running max is
 // carried across batches by rescaling (one memory round trip per batch).
-__device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long mb, int r, int col4) {
-  const int rpb = a.rows_per_block;
+//
+// A merged block: where its pieces' slots start, how many there are, and
+// which rows of the output they belong to.
+struct MergeBlock {
+  long long slot0;  // first slot of the block's pieces
+  long long row0;   // output row that the block's row base counts from
+  int n_split;      // pieces
+  int row_base;     // the block's first row, counted from row0
+  int R;            // rows below this bound (counted from row0) exist
+};
+
+// Merged block mb of a uniform batch: the full row blocks of every tree
+// (when they are cut), then the partial last blocks.
+__device__ __forceinline__ MergeBlock merge_block(const AttnArgs& a, long long mb) {
   const long long full_blocks = a.split_full > 1 ? static_cast<long long>(a.B) * a.full_rb : 0;
-  int rb, n_split, R;
-  long long slot0, row0;
-  if (a.req) {
-    const int bq = find_request(a.req, a.B, kReqMerge0, mb);
-    const int32_t* rec = a.req + bq * kReqFields;
-    const int m = static_cast<int>(mb - rec[kReqMerge0]);
-    const int bsplit = rec[kReqBSplit];
-    const int body_merges = bsplit > 1 ? rec[kReqNBlk] - 1 : 0;
-    if (m < body_merges) {  // a row block before the last
-      rb = m;
-      n_split = bsplit;
-      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(m) * bsplit;
-    } else {  // the last row block
-      rb = rec[kReqNBlk] - 1;
-      n_split = rec[kReqTSplit];
-      slot0 = static_cast<long long>(rec[kReqSlot0]) + static_cast<long long>(body_merges) * bsplit;
-    }
-    R = rec[kReqQLen] * a.H;
-    row0 = static_cast<long long>(rec[kReqQStart]) * a.H;
-  } else if (mb < full_blocks) {
-    const int b = static_cast<int>(mb / a.full_rb);
+  MergeBlock k;
+  int b, rb;
+  if (mb < full_blocks) {
+    b = static_cast<int>(mb / a.full_rb);
     rb = static_cast<int>(mb % a.full_rb);
-    n_split = a.split_full;
-    slot0 = mb * a.split_full;
-    R = a.R;
-    row0 = static_cast<long long>(b) * a.R;
+    k.n_split = a.split_full;
+    k.slot0 = mb * a.split_full;
   } else {
-    const int b = static_cast<int>(mb - full_blocks);
+    b = static_cast<int>(mb - full_blocks);
     rb = a.n_rb - 1;
-    n_split = a.split_tail;
-    slot0 = (a.split_full > 1 ? full_blocks * a.split_full : 0) + static_cast<long long>(b) * a.split_tail;
-    R = a.R;
-    row0 = static_cast<long long>(b) * a.R;
+    k.n_split = a.split_tail;
+    k.slot0 = (a.split_full > 1 ? full_blocks * a.split_full : 0) + static_cast<long long>(b) * a.split_tail;
   }
-  const int row = rb * rpb + r;
-  if (row >= R) return;
+  k.R = a.R;
+  k.row0 = static_cast<long long>(b) * a.R;
+  k.row_base = rb * a.rows_per_block;
+  return k;
+}
+
+// Row r of merged block k, float4 column col4: the pieces' partial outputs
+// combined by log-sum-exp (online rescaled, eight pieces' loads at a time).
+__device__ __forceinline__ void merge_row(const AttnArgs& a, int d_c, const MergeBlock& k, int r, int col4) {
+  const int rpb = a.rows_per_block;
+  const int row = k.row_base + r;
+  if (row >= k.R) return;
   constexpr int kBatch = 8;
   float M = -INFINITY, W = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+  for (int s0 = 0; s0 < k.n_split; s0 += kBatch) {
     float l[kBatch], m[kBatch];
     float4 v[kBatch];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const long long sr = (slot0 + s0 + k) * rpb + r;
-      const bool in = s0 + k < n_split;
-      l[k] = in ? a.ws_l[sr] : 0.f;
-      m[k] = in ? a.ws_m[sr] : 0.f;
-      v[k] = in ? *reinterpret_cast<const float4*>(a.ws_o + sr * d_c + col4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < kBatch; ++j) {
+      const long long sr = (k.slot0 + s0 + j) * rpb + r;
+      const bool in = s0 + j < k.n_split;
+      l[j] = in ? a.ws_l[sr] : 0.f;
+      m[j] = in ? a.ws_m[sr] : 0.f;
+      v[j] = in ? *reinterpret_cast<const float4*>(a.ws_o + sr * d_c + col4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     // pieces with no visible key (row sum 0) add nothing
     float mb_max = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) mb_max = l[k] > 0.f ? fmaxf(mb_max, m[k]) : mb_max;
+    for (int j = 0; j < kBatch; ++j) mb_max = l[j] > 0.f ? fmaxf(mb_max, m[j]) : mb_max;
     if (mb_max == -INFINITY) continue;
     const float Mn = fmaxf(M, mb_max);
     const float sc = expf(M - Mn);  // 0 on the first batch with a visible key
@@ -482,52 +492,70 @@ __device__ __forceinline__ void merge_one(const AttnArgs& a, int d_c, long long 
     acc.z *= sc;
     acc.w *= sc;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const float w = l[k] > 0.f ? l[k] * expf(m[k] - Mn) : 0.f;
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = l[j] > 0.f ? l[j] * expf(m[j] - Mn) : 0.f;
       W += w;
-      acc.x = fmaf(w, v[k].x, acc.x);
-      acc.y = fmaf(w, v[k].y, acc.y);
-      acc.z = fmaf(w, v[k].z, acc.z);
-      acc.w = fmaf(w, v[k].w, acc.w);
+      acc.x = fmaf(w, v[j].x, acc.x);
+      acc.y = fmaf(w, v[j].y, acc.y);
+      acc.z = fmaf(w, v[j].z, acc.z);
+      acc.w = fmaf(w, v[j].w, acc.w);
     }
     M = Mn;
   }
   const float inv = 1.f / W;
-  const long long grow = row0 + row;
+  const long long grow = k.row0 + row;
   *reinterpret_cast<float4*>(a.out + grow * d_c + col4 * 4) =
       make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   if (col4 == 0 && a.lse) a.lse[grow] = M + logf(W);
 }
 
-// Threads cover the rows that exist: a uniform batch's merged full row blocks
-// (rows_per_block rows each), then its merged partial last blocks (R - (n_rb
-// - 1) rows_per_block rows each); a ragged batch's merged blocks (count from
-// its records) at rows_per_block rows each, rows past a request's end
-// returning at once.  The grid strides over them.
+// Uniform batch: threads cover the rows that exist, the merged full row
+// blocks (rows_per_block rows each) and then the merged partial last blocks
+// (R - (n_rb - 1) rows_per_block rows each); the grid strides over them.  The
+// block of an element follows from its index by division.
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int d_c, long long n_blocks) {
   const int cpt = d_c / 4;
   const int rpb = a.rows_per_block;
-  long long full_blocks, tail_rows;
-  if (a.req) {
-    full_blocks = req_totals(a.req, a.B)[kTotMerge];
-    tail_rows = rpb;
-  } else {
-    full_blocks = a.split_full > 1 ? static_cast<long long>(a.B) * a.full_rb : 0;
-    tail_rows = a.R - static_cast<long long>(a.n_rb - 1) * rpb;
-  }
-  const long long tail_blocks = a.req ? 0 : n_blocks - full_blocks;
+  const long long full_blocks = a.split_full > 1 ? static_cast<long long>(a.B) * a.full_rb : 0;
+  const long long tail_rows = a.R - static_cast<long long>(a.n_rb - 1) * rpb;
   const long long full_rows = full_blocks * rpb;
-  const long long total = (full_rows + tail_blocks * tail_rows) * cpt;
+  const long long total = (full_rows + (n_blocks - full_blocks) * tail_rows) * cpt;
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
   for (long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
     const int col4 = static_cast<int>(idx % cpt);
     const long long row_i = idx / cpt;
     if (row_i < full_rows) {
-      merge_one(a, d_c, row_i / rpb, static_cast<int>(row_i % rpb), col4);
+      merge_row(a, d_c, merge_block(a, row_i / rpb), static_cast<int>(row_i % rpb), col4);
     } else {
       const long long t = row_i - full_rows;
-      merge_one(a, d_c, full_blocks + t / tail_rows, static_cast<int>(t % tail_rows), col4);
+      merge_row(a, d_c, merge_block(a, full_blocks + t / tail_rows), static_cast<int>(t % tail_rows), col4);
     }
+  }
+}
+
+// Ragged batch: a workgroup takes tasks of 256 / (d_c / 4) rows of one merged
+// block.  The prep kernel wrote each merged block's slots and rows into the
+// merge table, so a task needs one 16-byte load before its pieces' loads.
+// Tasks are numbered block after block up to the real number of merged blocks
+// (from the records); the grid strides over them.
+__global__ __launch_bounds__(256) void attn_merge_ragged_kernel(AttnArgs a, int d_c) {
+  const int cpt = d_c / 4;
+  const int task_rows = blockDim.x / cpt;
+  const int tasks_per_block = (a.rows_per_block + task_rows - 1) / task_rows;
+  const long long n_tasks = static_cast<long long>(req_totals(a.req, a.B)[kTotMerge]) * tasks_per_block;
+  const int r_in = static_cast<int>(threadIdx.x) / cpt;
+  const int col4 = static_cast<int>(threadIdx.x) % cpt;
+  if (r_in >= task_rows) return;  // only when d_c / 4 does not divide 256 (no barrier below)
+  for (long long t = blockIdx.x; t < n_tasks; t += gridDim.x) {
+    const int r = static_cast<int>(t % tasks_per_block) * task_rows + r_in;
+    const int4 e = a.merge_tab[t / tasks_per_block];
+    MergeBlock k;
+    k.slot0 = e.x;
+    k.n_split = e.y;
+    k.row0 = e.z;
+    k.row_base = 0;
+    k.R = e.w;
+    if (r < a.rows_per_block) merge_row(a, d_c, k, r, col4);
   }
 }
 
@@ -536,17 +564,23 @@ hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const Attn
                  : plan.kernel == AttnKernel::kMfmaF32 ? launch_attn_mfma_f32(s, plan, a, stream)
                                                        : launch_attn_valu(s, plan, a, stream);
   if (e != hipSuccess || plan.merge_blocks == 0) return e;
-  long long rows;
   if (a.req) {
-    rows = plan.merge_blocks * plan.rows_per_block;  // an upper bound; the grid strides
-  } else {
-    const long long full_blocks = plan.split_full > 1 ? static_cast<long long>(s.B) * plan.full_rb : 0;
-    const long long tail_rows = static_cast<long long>(s.q_len) * s.H - static_cast<long long>(plan.n_rb - 1) *
-                                                                          plan.rows_per_block;
-    rows = full_blocks * plan.rows_per_block + (plan.merge_blocks - full_blocks) * tail_rows;
+    // The tasks of the bound (merged blocks x tasks per block), at most 8
+    // workgroups per CU: the bound can far exceed the real count, and every
+    // workgroup past it still reads the count before it leaves (measured:
+    // 16384 workgroups cost ~7 us more than 2048 at 32 real merged blocks).
+    // The kernel strides over the real count.
+    const int task_rows = 256 / (s.d_c / 4);
+    long long grid = plan.merge_blocks * ((plan.rows_per_block + task_rows - 1) / task_rows);
+    if (grid > 8 * kNumCU) grid = 8 * kNumCU;
+    attn_merge_ragged_kernel<<<dim3(static_cast<unsigned>(grid)), 256, 0, stream>>>(a, s.d_c);
+    return hipGetLastError();
   }
-  long long grid = (rows * (s.d_c / 4) + 255) / 256;
-  if (a.req && grid > 8 * kNumCU) grid = 8 * kNumCU;
+  const long long full_blocks = plan.split_full > 1 ? static_cast<long long>(s.B) * plan.full_rb : 0;
+  const long long tail_rows =
+      static_cast<long long>(s.q_len) * s.H - static_cast<long long>(plan.n_rb - 1) * plan.rows_per_block;
+  const long long rows = full_blocks * plan.rows_per_block + (plan.merge_blocks - full_blocks) * tail_rows;
+  const long long grid = (rows * (s.d_c / 4) + 255) / 256;
   attn_merge_kernel<<<dim3(static_cast<unsigned>(grid)), 256, 0, stream>>>(a, s.d_c, plan.merge_blocks);
   return hipGetLastError();
 }
@@ -556,7 +590,7 @@ hipError_t launch_ragged_prep(const AttnShape& s, const AttnPlan& plan, const At
   ragged_prep_kernel<<<dim3(1), kPrepThreads, 0, stream>>>(prefix_len, q_len, s.B, s.H, s.q_len, s.kv_len,
                                                            plan.rows_per_block, static_cast<int>(plan.target),
                                                            static_cast<int>(plan.n_slots),
-                                                           plan.kernel == AttnKernel::kMfmaF32 ? kPlanCostF32
+                                                           static_cast<int>(plan.merge_blocks), plan.kernel == AttnKernel::kMfmaF32 ? kPlanCostF32
                                                                                                : kPlanCostDefault,
                                                            const_cast<int32_t*>(a.req));
   return hipGetLastError();

@@ -107,7 +107,8 @@ struct AttnArgs {
   // Ragged batches (per-request lengths, on the device): req points at the
   // request records the prep kernel wrote (null for a uniform batch).
   const int32_t* req;
-  int kv_stride;  // cache rows per request
+  const int4* merge_tab;  // the merge table after the records (MergeField order)
+  int kv_stride;          // cache rows per request
 };
 
 // Records of a ragged batch, written by the prep kernel into the workspace
@@ -138,6 +139,17 @@ __host__ __device__ inline const int32_t* req_totals(const int32_t* rq, int B) {
   return rq + B * kReqFields + 4 * B;
 }
 __host__ __device__ inline size_t req_words(int B) { return static_cast<size_t>(B) * (kReqFields + 4) + kReqTotals; }
+// After the records, at the next 16-byte boundary, the merge table: one entry
+// per merged row block (a row block whose kv range was cut into pieces), in
+// merged-block order.
+enum MergeField : int {
+  kMtSlot0 = 0,  // first slot of the block's pieces
+  kMtSplit,      // pieces
+  kMtRow0,       // first output row (packed node * H + head)
+  kMtRows,       // rows of the block that exist
+  kMtFields
+};
+__host__ __device__ inline size_t merge_table_word0(int B) { return (req_words(B) + 3) & ~static_cast<size_t>(3); }
 
 // Planning of a ragged batch, in tiles of 32 keys (every kernel's tile).  A
 // unit costs its tiles plus a set-up (tree masks, queries, first tile,
