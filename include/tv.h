@@ -160,8 +160,9 @@ size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_
  *   [B][kv_stride][d_r] (kv_dtype), rope slices already rotated.
  *   Workspace (device, 16-byte aligned, caller-owned, reused across calls on
  *   one stream): at least tv_verify_attn_ragged_workspace_size(...) bytes; it
- *   always holds the per-request records a small prep kernel writes from the
- *   device lengths, then the split partials.  Launch sizes come from the
+ *   always holds the per-request records and the merge table (the slots and
+ *   rows of each row block cut into kv pieces) that a small prep kernel
+ *   writes from the device lengths, then the split partials.  Launch sizes come from the
  *   bounds, so nothing is read back to the host and the call can be captured
  *   in a graph.  1 <= max_q_len <= TV_MAX_Q_LEN; kv_stride >= max_q_len;
  *   other limits as for tv_verify_attn with prefix_len = kv_stride -
