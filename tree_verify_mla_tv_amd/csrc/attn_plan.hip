@@ -174,6 +174,7 @@ __device__ __forceinline__ ReqLen req_len(const int32_t* prefix_len, const int32
 
 constexpr int kPrepThreads = 1024;
 constexpr int kSortMax = 4096;  // classes sorted in LDS (B <= 2048); larger batches keep request order
+constexpr int kRankSortMax = 256;  // up to this many classes by rank (two barriers), more by a bitonic network
 
 // Sum over the workgroup (ends with every thread holding the total).
 __device__ long long block_sum(long long v, long long* s_part) {
@@ -277,19 +278,46 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
     atomicAdd(&s_hist[c][plan_bucket(last_t + cost.setup)], 1);
   }
   __syncthreads();
-  if (t < kPlanCands) {
-    const long long units = static_cast<long long>(s_units[t]);
-    s_est[t] = static_cast<long long>(s_pieces[t]) > max_slots || units == 0
-                   ? (t == 0 ? 0.0 : -1.0)
-                   : plan_estimate(Wt + cost.setup * units, units, s_dmin[t], s_dmax[t],
-                                   static_cast<long long>(s_pieces[t]), cost.pieces_per_step, s_hist[t], target);
+  // One wave per candidate.  Lane i holds bucket 63 - i; an inclusive scan
+  // over the lanes gives each bucket's count of units that long or longer,
+  // and the lowest lane where it reaches target + 1 names the bucket of the
+  // (target+1)-th longest unit.
+  {
+    const int wave = t >> 6, lane = t & 63;
+    for (int c = wave; c < kPlanCands; c += kPrepThreads / 64) {
+      long long cum = s_hist[c][63 - lane];
+      for (int d = 1; d < 64; d <<= 1) {
+        const long long o = __shfl_up(cum, d);
+        if (lane >= d) cum += o;
+      }
+      const unsigned long long hit = __ballot(cum >= static_cast<long long>(target) + 1);
+      if (lane == 0) {
+        const long long units = static_cast<long long>(s_units[c]);
+        const long long pieces = static_cast<long long>(s_pieces[c]);
+        const int k2 = units > target && hit ? 63 - (__ffsll(static_cast<long long>(hit)) - 1) : -1;
+        s_est[c] = pieces > max_slots || units == 0
+                       ? (c == 0 ? 0.0 : -1.0)
+                       : plan_estimate(Wt + cost.setup * units, s_dmin[c], s_dmax[c], pieces, cost.pieces_per_step,
+                                       k2, target);
+      }
+    }
   }
   __syncthreads();
-  if (t == 0) {
-    int best = 0;
-    for (int c = 1; c < kPlanCands; ++c)
-      if (s_est[c] >= 0.0 && s_est[c] < s_est[best]) best = c;
-    s_choice = best;
+  // The least estimate among the candidates within the slot budget (negative
+  // marks the others; the uncut candidate 0 always qualifies), the lowest
+  // index among equals: a reduction across wave 0.
+  if (t < 64) {
+    double v = t < kPlanCands && s_est[t] >= 0.0 ? s_est[t] : INFINITY;
+    int c = t;
+    for (int d = 32; d >= 1; d >>= 1) {
+      const double ov = __shfl_xor(v, d);
+      const int oc = __shfl_xor(c, d);
+      if (ov < v || (ov == v && oc < c)) {
+        v = ov;
+        c = oc;
+      }
+    }
+    if (t == 0) s_choice = c;
   }
   __syncthreads();
   const int cap_b = s_capb[s_choice], cap_t = s_capt[s_choice];
@@ -357,7 +385,25 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
     }
   };
   int n_sort = 1;
-  if (sorted) {
+  if (sorted && n_cls <= kRankSortMax) {
+    // Keys are distinct (the id is in the low bits): each class's position is
+    // the number of smaller keys.
+    unsigned long long key = 0;
+    if (t < n_cls) {
+      int units, len;
+      cls_of(t, units, len);
+      key = (static_cast<unsigned long long>(0xffffffffu - static_cast<unsigned>(units ? len : 0)) << 32) |
+            static_cast<unsigned>(t);
+      s_sort[t] = key;
+    }
+    __syncthreads();
+    int rank = 0;
+    if (t < n_cls)
+      for (int j = 0; j < n_cls; ++j) rank += s_sort[j] < key ? 1 : 0;
+    __syncthreads();
+    if (t < n_cls) s_sort[rank] = key;
+    __syncthreads();
+  } else if (sorted) {
     while (n_sort < n_cls) n_sort <<= 1;
     for (int i = t; i < n_sort; i += kPrepThreads) {
       unsigned long long key = ~0ull;

@@ -227,21 +227,16 @@ __host__ __device__ inline long long plan_bucket_lo(int k) { return (static_cast
 // unit, and with more units than workgroups at least the longest unit plus the
 // (M+1)-th longest (some workgroup runs two); plus the merge pass, one
 // tile-step of the whole GPU per pieces_per_step pieces.
-__host__ __device__ inline double plan_estimate(long long work, long long units, long long d_min, long long d_max,
-                                                long long pieces, int pieces_per_step, const int* hist,
-                                                long long M) {
+// k2 is the bucket of the (M+1)-th longest unit (the longest bucket k whose
+// units and all longer ones number at least M + 1), or -1 when there are at
+// most M units.
+__host__ __device__ inline double plan_estimate(long long work, long long d_min, long long d_max, long long pieces,
+                                                int pieces_per_step, int k2, long long M) {
   double e = static_cast<double>(work) / M + 0.5 * d_min;
   e = e > d_max ? e : static_cast<double>(d_max);
-  if (units > M) {
-    long long cum = 0;
-    for (int k = 63; k >= 0; --k) {
-      cum += hist[k];
-      if (cum >= M + 1) {
-        const double two = static_cast<double>(d_max + plan_bucket_lo(k));
-        e = e > two ? e : two;
-        break;
-      }
-    }
+  if (k2 >= 0) {
+    const double two = static_cast<double>(d_max + plan_bucket_lo(k2));
+    e = e > two ? e : two;
   }
   return e + static_cast<double>(pieces) / pieces_per_step;
 }
