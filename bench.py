@@ -355,7 +355,9 @@ def main() -> int:
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step(ev0=None, ev1=None):
+    def step(evr=None, ev0=None, ev1=None):
+        if evr is not None:
+            evr.record()
         tv.tree_rope(q_rope, k_rope, parent, P, w.theta)
         if ev0 is not None:
             ev0.record()
@@ -367,15 +369,16 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        step(e0, e1)
+    for er, e0, e1 in evs:
+        step(er, e0, e1)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    attn_ms = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in evs]))
+    rope_ms = float(np.mean([er.elapsed_time(e0) for er, e0, _ in evs]))
 
     counts = algorithmic_counts(w, inp["parent"])
     kern = KERNELS[w.kv_dtype]
@@ -411,12 +414,17 @@ def main() -> int:
             "traffic": traffic,
             "avg_launch_ms": round(attn_ms, 5),
             "timed": "HIP events on the launch stream around each verify_attn call: the attention kernel and "
-                     "its split-kv merge pass (about 14 us of the call), so the rate is slightly conservative",
+                     "its split-kv merge pass (about 9 us of the call), so the rate is slightly conservative",
             "algorithmic_flops": counts["flops"],
             "algorithmic_bytes": counts["attn_bytes"],
             "achieved_hbm_gbs": round(counts["attn_bytes"] / (attn_ms * 1e-3) / 1e9, 1),
         },
     }
+    # The step's RoPE (the queries and the tree's own key rows), timed by HIP
+    # events around each tree_rope call of the same timed steps.
+    rec["rope"] = {"kernel": "tree_rope_kernel", "ms": round(rope_ms, 5), "bytes": counts["rope_bytes"],
+                   "achieved_gbs": round(counts["rope_bytes"] / (rope_ms * 1e-3) / 1e9, 1),
+                   "frac_of_hbm_peak": round(counts["rope_bytes"] / (rope_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if w.kv_dtype == "bf16":
         rec["roofline"]["reference_gemm"] = reference_gemm(torch)
     if args.cpu_sample > 0:
