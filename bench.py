@@ -83,8 +83,14 @@ def cpu_baseline(inp, w, n_sample: int) -> dict:
                   w.prefix_len, w.theta, w.sm_scale, w.kv_dtype)
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": round(1.0 / (dt * w.B / n_sample), 6), "unit": "calls/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"float64 numpy oracle (RoPE + attention) on {n_sample} of {w.B} trees of the same batch, "
                       f"{dt:.2f} s, scaled x{w.B / n_sample:g} to one call; host CPUs available: "
                       f"{len(os.sched_getaffinity(0))}"}
