@@ -89,7 +89,8 @@ def cpu_baseline(inp, w, n_sample: int) -> dict:
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
     except OSError:
         pass
-    return {"value": round(1.0 / (dt * w.B / n_sample), 6), "unit": "calls/s", "cores": threads,
+    return {"value": round(1.0 / (dt * w.B / n_sample), 6), "seconds_per_call": round(dt * w.B / n_sample, 3),
+            "unit": "calls/s", "cores": threads,
             "kind": "oracle", "cpu_model": model,
             "sample": f"float64 numpy oracle (RoPE + attention) on {n_sample} of {w.B} trees of the same batch, "
                       f"{dt:.2f} s, scaled x{w.B / n_sample:g} to one call; host CPUs available: "
@@ -210,11 +211,27 @@ def reference_gemm(torch, n: int = 8192, reps: int = 10) -> dict:
             "frac_of_peak": round(tf / PEAKS_TFLOPS["bf16"], 4)}
 
 
-def fp32_configs(torch, tv, W) -> dict:
+def cpu_baseline_fp32(w, inp) -> float:
+    """The oracle as it stands on one fp32 configuration's whole call (inputs
+    already rotated, as the GPU timing has them): median of 5, microseconds."""
+    import numpy as np
+    from oracle import tv_oracle as O
+    args = (O.as_f64(inp["q_lat"], "f32"), O.as_f64(inp["q_rope"], "f32"), O.as_f64(inp["c_kv"], "f32"),
+            O.as_f64(inp["k_rope"], "f32"), inp["parent"], w.prefix_len, w.sm_scale)
+    times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        O.verify_attn(*args)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)) * 1e6
+
+
+def fp32_configs(torch, tv, W, with_oracle: bool = False) -> dict:
     """The fp32-cache configurations: microseconds per verify_attn call
     (inputs already rotated; the fp32 matrix-core kernel at d_c 512 / d_r 64,
     the VALU kernel at 64 / 32), TFLOP/s against the fp32 peak (157.3 for
-    both) and GB/s, from the algorithmic counts."""
+    both) and GB/s, from the algorithmic counts; with_oracle adds the float64
+    oracle's time for the same call on the host (median of 5) and the ratio."""
     import numpy as np
     dev = "cuda:0"
     out = {}
@@ -237,6 +254,10 @@ def fp32_configs(torch, tv, W) -> dict:
                      "frac_of_fp32_peak": round(c["flops"] / (ms * 1e-3) / 1e12 / PEAKS_TFLOPS["f32_mfma"], 4),
                      "kernel": "attn_mfma_f32_kernel" if (w.d_c, w.d_r) == (512, 64) else "attn_valu_kernel",
                      "gbs": round(c["attn_bytes"] / (ms * 1e-3) / 1e9, 1)}
+        if with_oracle:
+            cpu_us = cpu_baseline_fp32(w, inp)
+            out[name]["cpu_oracle_us"] = round(cpu_us, 1)
+            out[name]["gpu_over_oracle"] = round(cpu_us / (ms * 1e3), 1)
     return out
 
 
@@ -435,10 +456,11 @@ def main() -> int:
         rec["roofline"]["reference_gemm"] = reference_gemm(torch)
     if args.cpu_sample > 0:
         rec["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_sample, w.B))
+        rec["cpu_baseline"]["gpu_over_oracle"] = round(value / rec["cpu_baseline"]["value"], 1)
     if args.next_rows and w.kv_dtype == "bf16":
         rec["next_rows"] = next_rows(torch, tv, W, inp, w, c_kv, k_rope, parent, args.cpu_sample > 0)
         rec["next_rows"]["verify_variants"] = verify_variants(torch, tv, W)
-        rec["next_rows"]["fp32_configs"] = fp32_configs(torch, tv, W)
+        rec["next_rows"]["fp32_configs"] = fp32_configs(torch, tv, W, args.cpu_sample > 0)
     print(json.dumps(rec), flush=True)
     return 0
 
