@@ -113,3 +113,53 @@ def test_ragged_graph_replays_with_new_lengths():
         call(out_e, ws_e)
         torch.cuda.synchronize()
         assert torch.equal(out_g[:n], out_e[:n]), rep
+
+
+def test_ragged_step_graph_replays():
+    """The whole ragged step (tree RoPE in place, then attention) captured
+    once; before each replay and each eager call the caches and queries are
+    restored, so every replay must equal the eager step: output, rotated
+    queries and rotated tree key rows."""
+    rng = np.random.default_rng(13)
+    B, H, max_q, S, d_c, d_r = 6, 16, 17, 3000, 512, 64
+    N = B * max_q
+    q_lat = torch.empty(N, H, d_c, device="cuda")
+    q_rope = torch.empty(N, H, d_r, device="cuda")
+    c_kv = _bf16(rng.standard_normal((B, S, d_c), dtype=np.float32) * 0.5)
+    k_rope = _bf16(rng.standard_normal((B, S, d_r), dtype=np.float32) * 0.5)
+    k0 = k_rope.clone()
+    parent = torch.empty(N, dtype=torch.int32, device="cuda")
+    pl = torch.empty(B, dtype=torch.int32, device="cuda")
+    ql = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws_n = tv.load().tv_verify_attn_ragged_workspace_size(B, H, max_q, S, d_c, d_r, tv.TV_BF16)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    out = torch.zeros_like(q_lat)
+    step = lambda: tv.verify_step_ragged(q_lat, q_rope, c_kv, k_rope, parent, pl, ql, max_q, 10000.0, 0.04, out=out,
+                                         workspace=ws)
+
+    def fill(seed):
+        r = np.random.default_rng(seed)
+        q_lens = [int(x) for x in r.integers(1, max_q + 1, B)]
+        pars = np.concatenate([W.tree_branch(q, r).astype(np.int32) for q in q_lens])
+        par = np.zeros(N, np.int32)
+        par[:len(pars)] = pars
+        parent.copy_(torch.from_numpy(par))
+        pl.copy_(torch.tensor([int(x) for x in r.integers(0, S - max_q, B)], dtype=torch.int32))
+        ql.copy_(torch.tensor(q_lens, dtype=torch.int32))
+        q_lat.copy_(torch.from_numpy(r.standard_normal((N, H, d_c), dtype=np.float32)))
+        q_rope.copy_(torch.from_numpy(r.standard_normal((N, H, d_r), dtype=np.float32)))
+        k_rope.copy_(k0)
+        return sum(q_lens)
+
+    fill(0)
+    graph = _capture(step)
+    for rep in range(3):
+        n = fill(300 + rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out[:n].clone(), q_rope[:n].clone(), k_rope.clone())
+        fill(300 + rep)
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], out[:n]) and torch.equal(got[1], q_rope[:n]) and torch.equal(got[2], k_rope), rep
+        assert not torch.equal(k_rope, k0), rep  # the tree key rows were rotated
