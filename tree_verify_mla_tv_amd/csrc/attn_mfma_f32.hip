@@ -268,18 +268,8 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
   // Row sum over the four lane groups that share the row.
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (!row_valid) return;  // no barrier follows
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  float* dst = w.slot < 0 ? a.out + (w.row0 + row) * DC
-                          : a.ws_o + (w.slot * kF32Rows + r_blk) * DC;
-  // Register v of block 4 m + r holds d = 64 m + 4 (4 lg + v) + r of row ln.
-#pragma unroll
-  for (int m = 0; m < DC / 64; ++m)
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      *reinterpret_cast<float4*>(dst + 64 * m + 16 * lg + 4 * v) =
-          make_float4(o[4 * m][v] * inv, o[4 * m + 1][v] * inv, o[4 * m + 2][v] * inv, o[4 * m + 3][v] * inv);
-  if (lg == 0) {
+  if (row_valid && lg == 0) {
     if (w.slot < 0) {
       if (a.lse) a.lse[w.row0 + row] = (m_ref + log2f(l_tot)) * kLn2;
     } else {
@@ -287,6 +277,31 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
       a.ws_m[srow] = m_ref * kLn2;
       a.ws_l[srow] = l_tot;
     }
+  }
+  // Output through LDS, so that each store instruction writes 1 KB of
+  // consecutive bytes (written straight from the accumulators, a store
+  // touched 16 B in each of 64 places).  The tile buffers are free: every wave
+  // has passed a barrier since its last read of them.  Register v of block
+  // 4 m + r holds d = 64 m + 4 (4 lg + v) + r of row ln; a row's staging
+  // pitch of 516 floats puts the 16 rows a store serves in distinct banks.
+  constexpr int kOutStride = DC + 4;
+  static_assert(kF32Rows * kOutStride <= 2 * kTileFloats, "the output block fits the tile buffers");
+  float* const so = sK;
+#pragma unroll
+  for (int m = 0; m < DC / 64; ++m)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      *reinterpret_cast<float4*>(so + r_blk * kOutStride + 64 * m + 16 * lg + 4 * v) =
+          make_float4(o[4 * m][v] * inv, o[4 * m + 1][v] * inv, o[4 * m + 2][v] * inv, o[4 * m + 3][v] * inv);
+  __syncthreads();
+  const int rows = min(kF32Rows, w.R - w.rb * kF32Rows);  // rows of the block that exist
+  float* const dst = w.slot < 0 ? a.out + (w.row0 + static_cast<int64_t>(w.rb) * kF32Rows) * DC
+                                : a.ws_o + w.slot * kF32Rows * DC;
+  for (int idx = threadIdx.x; idx < rows * (DC / 4); idx += kF32Threads) {
+    const int r = idx / (DC / 4);
+    const int c4 = idx - r * (DC / 4);
+    *reinterpret_cast<float4*>(dst + static_cast<int64_t>(r) * DC + 4 * c4) =
+        *reinterpret_cast<const float4*>(so + r * kOutStride + 4 * c4);
   }
 }
 
