@@ -74,7 +74,8 @@ def algorithmic_counts(w, parent) -> dict:
 
 
 def cpu_baseline(inp, w, n_sample: int) -> dict:
-    """The oracle as it stands, on the first n_sample trees of the same batch."""
+    """The oracle as it stands, on the first n_sample trees of the same batch
+    (the whole batch, i.e. one whole call, by default)."""
     import threadpoolctl
     from oracle import tv_oracle as O
     s = slice(0, n_sample)
@@ -92,9 +93,11 @@ def cpu_baseline(inp, w, n_sample: int) -> dict:
     return {"value": round(1.0 / (dt * w.B / n_sample), 6), "seconds_per_call": round(dt * w.B / n_sample, 3),
             "unit": "calls/s", "cores": threads,
             "kind": "oracle", "cpu_model": model,
-            "sample": f"float64 numpy oracle (RoPE + attention) on {n_sample} of {w.B} trees of the same batch, "
-                      f"{dt:.2f} s, scaled x{w.B / n_sample:g} to one call; host CPUs available: "
-                      f"{len(os.sched_getaffinity(0))}"}
+            "sample": (f"float64 numpy oracle (RoPE + attention), one whole call (all {w.B} trees), {dt:.2f} s"
+                       if n_sample == w.B else
+                       f"float64 numpy oracle (RoPE + attention) on {n_sample} of {w.B} trees of the same batch, "
+                       f"{dt:.2f} s, scaled x{w.B / n_sample:g} to one call")
+                      + f"; host CPUs available: {len(os.sched_getaffinity(0))}"}
 
 
 def load_traffic(kernel: dict, workload: str):
@@ -326,7 +329,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-sample", type=int, default=6, help="trees the CPU oracle times (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 30,
+                    help="trees the CPU oracle times (default: the whole batch, one call; 0 = skip)")
     ap.add_argument("--no-next-rows", dest="next_rows", action="store_false",
                     help="skip timing the steps after verify (greedy tokens, tree accept, KV compaction)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -375,7 +379,7 @@ def main() -> int:
     parent = torch.from_numpy(inp["parent"]).to(dev)
     P = w.prefix_len
     if P > 0:
-        tv.rope_neox(k_rope[:, :P, :], None, w.theta)  # cache fill, outside the timed region
+        tv.rope_neox_strided(k_rope[:, :P, :], None, w.theta)  # cache fill, outside the timed region
     out = torch.empty_like(q_lat)
     dt_code = tv.TV_BF16 if w.kv_dtype == "bf16" else tv.TV_F32
     ws_bytes = tv.workspace_size(w.B, w.H, w.q_len, P, w.d_c, w.d_r, dt_code)

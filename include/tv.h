@@ -83,19 +83,34 @@ tv_status_t tv_tree_positions(const int32_t* parent, int32_t B, int32_t q_len, i
  * tv_rope_neox — in-place NeoX rotary embedding with float64 angles.
  *   [RoPE page, "The Message", "The Float64 Decision", "What Input Knowledge
  *   Is Required" item 1]
+ *   x is viewed as [n_tok][n_head][d_r] elements of `dtype`: token t's heads
+ *   start at element t * tok_stride and are contiguous rows of d_r elements.
+ *   Token t turns at position p = pos[t] (pos: int32 [n_tok], device), or at
+ *   p = t when pos is NULL.  For k < d_r/2 the pair (x[k], x[k + d_r/2]) turns
+ *   by the angle p * inv_freq[k], inv_freq[k] = 1 / theta^(2k/d_r); angle,
+ *   cos, sin and the rotation are float64 and the result is rounded once
+ *   (nearest-even) to dtype.
+ *   d_r even, 2 <= d_r <= 128; n_tok >= 0 (0 = nothing to do); n_head >= 1;
+ *   tok_stride >= 0; theta > 0.  x 16-byte aligned, pos 4-byte aligned.
+ *   n_tok * n_head * d_r / 2 above 2^40 returns TV_ERR_UNSUPPORTED.
+ */
+tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int64_t n_tok, int32_t n_head,
+                         int32_t d_r, int64_t tok_stride, double theta, hipStream_t stream);
+
+/*
+ * tv_rope_neox_strided — tv_rope_neox over a batch of sequences, for strided
+ *   views such as a slice of a cache.  [RoPE page, as for tv_rope_neox]
  *   x is viewed as [n_seq][n_tok][n_head][d_r] elements of `dtype` with element
  *   strides seq_stride (between sequences) and tok_stride (between tokens);
  *   heads are contiguous rows of d_r elements.  Token t of sequence s turns at
- *   position p = pos[s * pos_seq_stride + t], or p = t when pos is NULL.
- *   For k < d_r/2 the pair (x[k], x[k + d_r/2]) turns by the angle
- *   p * inv_freq[k], inv_freq[k] = 1 / theta^(2k/d_r); angle, cos, sin and the
- *   rotation are float64 and the result is rounded once (nearest-even) to dtype.
+ *   position p = pos[s * pos_seq_stride + t], or p = t when pos is NULL; the
+ *   rotation is that of tv_rope_neox.
  *   d_r even, 2 <= d_r <= 128; n_seq, n_tok >= 0 (0 = nothing to do); n_head >= 1;
- *   theta > 0.
+ *   strides >= 0; theta > 0.
  */
-tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t n_seq, int32_t n_tok,
-                         int32_t n_head, int32_t d_r, int64_t seq_stride, int64_t tok_stride,
-                         int64_t pos_seq_stride, double theta, hipStream_t stream);
+tv_status_t tv_rope_neox_strided(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t n_seq, int32_t n_tok,
+                                 int32_t n_head, int32_t d_r, int64_t seq_stride, int64_t tok_stride,
+                                 int64_t pos_seq_stride, double theta, hipStream_t stream);
 
 /*
  * tv_verify_attn — tree-verify attention in MLA absorb form.
@@ -151,10 +166,14 @@ size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_
  *   (lengths outside are clamped into these bounds; q_len 0 means nothing to
  *   do).  Nodes are packed request after request: request b's nodes start at
  *   node s_b = q_len[0] + ... + q_len[b-1] in
- *     q_lat [N][H][d_c], q_rope [N][H][d_r] f32, parent [N] int32 (node
- *     indices local to the request, as for tv_verify_attn), out [N][H][d_c]
- *     f32, lse [N][H] f32 (optional), N = sum of q_len (rows past it are not
- *     touched);
+ *     q_lat [n_nodes][H][d_c], q_rope [n_nodes][H][d_r] f32, parent [n_nodes]
+ *     int32 (node indices local to the request, as for tv_verify_attn), out
+ *     [n_nodes][H][d_c] f32, lse [n_nodes][H] f32 (optional).
+ *   n_nodes (host value, >= 0) is the caller's row count of those buffers:
+ *   the kernels never touch a node at or past it.  If the device lengths sum
+ *   to more, the request that crosses n_nodes keeps only its nodes below it
+ *   and the requests after it get q_len 0 (their rows are not computed);
+ *   rows from the sum of the lengths up to n_nodes are not touched;
  *   the cache holds kv_stride rows per request, the first prefix_len[b] +
  *   q_len[b] of which are used: c_kv [B][kv_stride][d_c], k_rope
  *   [B][kv_stride][d_r] (kv_dtype), rope slices already rotated.
@@ -169,7 +188,8 @@ size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_
  *   max_q_len.
  */
 tv_status_t tv_verify_attn_ragged(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
-                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len,
+                                  int32_t n_nodes, int32_t B,
                                   int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
                                   tv_dtype_t kv_dtype, float sm_scale, float* out, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
@@ -179,10 +199,12 @@ tv_status_t tv_verify_attn_ragged(const float* q_lat, const float* q_rope, const
  *   query rows and tree key rows rotated in place at prefix_len[b] + depth
  *   (as tv_tree_rope does for one request), then tv_verify_attn_ragged.
  *   Arguments as for tv_verify_attn_ragged plus theta; q_rope and k_rope are
- *   modified.  The request records are computed once and serve both steps.
+ *   modified (only the rows of nodes below n_nodes after the clamp above).
+ *   The request records are computed once and serve both steps.
  */
 tv_status_t tv_verify_step_ragged(const float* q_lat, float* q_rope, const void* c_kv, void* k_rope,
-                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len,
+                                  int32_t n_nodes, int32_t B,
                                   int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
                                   tv_dtype_t kv_dtype, double theta, float sm_scale, float* out, float* lse,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -74,19 +74,28 @@ def estimate(work, units, d_min, d_max, pieces, per_step, hist, M):
     return e + float(pieces) / per_step
 
 
-def req_len(prefix, q_len, b, H, max_q, kv_stride, rpb):
-    q = min(max(q_len[b], 0), max_q)
-    P = min(max(prefix[b], 0), kv_stride - q)
-    return q, P, -(-(q * H) // rpb), -(-(P + q) // TILE)
+def clamp_lengths(prefix, q_len, max_q, kv_stride, n_nodes=None):
+    """Per request (q, P): q_len into [0, max_q]; then the packed nodes into
+    the caller's n_nodes rows (the request that crosses n_nodes keeps its nodes
+    below it, later requests none); prefix into [0, kv_stride - q]."""
+    out, start = [], 0
+    for b in range(len(q_len)):
+        q = min(max(q_len[b], 0), max_q)
+        qc = q if n_nodes is None else min(q, max(0, n_nodes - start))
+        start += q
+        out.append((qc, min(max(prefix[b], 0), kv_stride - qc)))
+    return out
 
 
-def plan(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=COST_DEFAULT):
+def plan(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=COST_DEFAULT, n_nodes=None):
     """The records: {"req": [dict per request], "cls_u0", "cls_id", "units",
-    "merges", "choice"}."""
+    "merges", "choice"}.  n_nodes: the caller's packed node rows (None: no
+    bound)."""
     SETUP, min_piece, per_step = cost
     B = len(q_len)
     _, max_slots, _ = launch_bounds(B, H, max_q, rpb, target)
-    rl = [req_len(prefix, q_len, b, H, max_q, kv_stride, rpb) for b in range(B)]
+    rl = [(q, P, -(-(q * H) // rpb), -(-(P + q) // TILE))
+          for q, P in clamp_lengths(prefix, q_len, max_q, kv_stride, n_nodes)]
     W0 = sum(nblk * (tiles + SETUP) for _, _, nblk, tiles in rl)
     Wt = sum(nblk * tiles for _, _, nblk, tiles in rl)
     T0 = max(1, W0 // target)

@@ -87,8 +87,25 @@ def test_workspace_size_is_a_function_of_shapes():
 
 
 def test_rope_rejects_before_launch():
-    lib = tv.load()
-    r = lib.tv_rope_neox
+    """tv_rope_neox(x, dtype, pos, n_tok, n_head, d_r, tok_stride, theta, stream)."""
+    r = tv.load().tv_rope_neox
+    assert r(A, 0, None, 0, 1, 64, 64, 1e4, None) == OK                  # nothing to do
+    assert r(None, 0, None, 5, 1, 64, 64, 1e4, None) == INV
+    assert r(A, 0, None, -1, 1, 64, 64, 1e4, None) == INV
+    assert r(A, 0, None, 5, 1, 63, 64, 1e4, None) == INV                  # odd d_r
+    assert r(A, 0, None, 5, 1, 256, 256, 1e4, None) == UNS                # d_r > 128
+    assert r(A, 0, None, 5, 0, 64, 64, 1e4, None) == INV
+    assert r(A, 0, None, 5, 1, 64, -1, 1e4, None) == INV                  # negative stride
+    assert r(A, 0, None, 5, 1, 64, 64, 0.0, None) == INV
+    assert r(A, 0, None, 5, 1, 64, 64, float("nan"), None) == INV
+    assert r(A, 2, None, 5, 1, 64, 64, 1e4, None) == INV                  # dtype
+    assert r(A + 4, 0, None, 5, 1, 64, 64, 1e4, None) == INV              # x not 16-byte aligned
+    assert r(A, 0, A + 2, 5, 1, 64, 64, 1e4, None) == INV                 # pos not 4-byte aligned
+    assert r(A, 0, None, 2**36, 64, 64, 4096, 1e4, None) == UNS           # 2^47 pairs: above the launch limit
+
+
+def test_rope_strided_rejects_before_launch():
+    r = tv.load().tv_rope_neox_strided
     assert r(A, 0, None, 0, 5, 1, 64, 0, 64, 0, 1e4, None) == OK          # nothing to do
     assert r(A, 0, None, 3, 0, 1, 64, 0, 64, 0, 1e4, None) == OK
     assert r(None, 0, None, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
@@ -100,6 +117,19 @@ def test_rope_rejects_before_launch():
     assert r(A, 2, None, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
     assert r(A + 4, 0, None, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
     assert r(A, 0, A + 2, 1, 5, 1, 64, 0, 64, 0, 1e4, None) == INV
+
+
+def test_rope_signature_matches_the_specified_boundary():
+    """The specified call: tv_rope_neox(x, dtype, pos, int64 n_tok, n_head,
+    d_r, int64 tok_stride, theta, stream) -- nine arguments, the token count
+    and stride 64-bit."""
+    import re as _re
+    text = open(HEADER).read()
+    m = _re.search(r"tv_status_t tv_rope_neox\((.*?)\);", text, flags=_re.S)
+    args = [a.strip() for a in m.group(1).split(",")]
+    assert [a.split()[-1].lstrip("*") for a in args] == ["x", "dtype", "pos", "n_tok", "n_head", "d_r", "tok_stride",
+                                                         "theta", "stream"]
+    assert args[3].startswith("int64_t") and args[6].startswith("int64_t")
 
 
 def test_tree_positions_rejects_before_launch():
@@ -191,10 +221,10 @@ def test_verify_attn_ragged_rejects_before_launch():
     f = lib.tv_verify_attn_ragged
 
     def call(**kw):
-        a = dict(q=A, p=A, B=3, H=8, mq=33, S=9000, d_c=512, d_r=64, dt=1, ws=A, ws_n=need)
+        a = dict(q=A, p=A, N=40, B=3, H=8, mq=33, S=9000, d_c=512, d_r=64, dt=1, ws=A, ws_n=need)
         a.update(kw)
-        return f(a["q"], A, A, A, A, a["p"], A, a["B"], a["H"], a["mq"], a["S"], a["d_c"], a["d_r"], a["dt"], 0.04,
-                 A, None, a["ws"], a["ws_n"], None)
+        return f(a["q"], A, A, A, A, a["p"], A, a["N"], a["B"], a["H"], a["mq"], a["S"], a["d_c"], a["d_r"],
+                 a["dt"], 0.04, A, None, a["ws"], a["ws_n"], None)
 
     assert call(S=20) == INV
     assert call(mq=257) == UNS
@@ -206,3 +236,5 @@ def test_verify_attn_ragged_rejects_before_launch():
     assert call(ws_n=need - 1) == INV
     assert call(ws=A + 8) == INV
     assert call(d_c=100) == UNS
+    assert call(N=-1) == INV                              # negative node count
+    assert call(N=2**28) == UNS                           # N * H rows past int32

@@ -99,7 +99,7 @@ def test_step_and_positions_big_tree():
     q_lat, q_rope, c_kv, k_rope, _ = _inputs(B, H, q, P, 512, 64, "bf16", "chain", seed=4)
     theta, sm = 10000.0, float(np.float32(1.0 / np.sqrt(576)))
     kr = _cache(k_rope, "bf16")
-    tv.rope_neox(kr[:, :P, :], None, theta)
+    tv.rope_neox_strided(kr[:, :P, :], None, theta)
     qr = torch.from_numpy(q_rope).cuda()
     out, lse = tv.verify_step(torch.from_numpy(q_lat).cuda(), qr, _cache(c_kv, "bf16"), kr,
                               torch.from_numpy(parent).cuda(), P, theta, sm, return_lse=True)

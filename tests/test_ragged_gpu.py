@@ -137,7 +137,7 @@ def test_ragged_step(dt):
     kr = _cache(k_rope, dt)
     for b, P in enumerate(prefixes):  # the cache's prefix rows were rotated when written
         if P:
-            tv.rope_neox(kr[b:b + 1, :P, :], None, theta)
+            tv.rope_neox_strided(kr[b:b + 1, :P, :], None, theta)
     qr = torch.from_numpy(q_rope).cuda()
     out, lse = tv.verify_step_ragged(torch.from_numpy(q_lat).cuda(), qr, _cache(c_kv, dt), kr,
                                      torch.from_numpy(parent).cuda(), torch.tensor(prefixes, dtype=torch.int32).cuda(),
@@ -260,3 +260,69 @@ def test_ragged_records_unsorted_large_batch():
                                O.as_f64(c_kv[b:b + 1, :P + q], "bf16"), O.as_f64(k_rope[b:b + 1, :P + q], "bf16"),
                                parent[None, s:s + q], P, sm)
         assert errors(out[s:s + q], ref[0])["max_rel"] <= TOL["bf16"]["max_rel"], b
+
+
+@pytest.mark.parametrize("step", [False, True])
+def test_ragged_lengths_past_node_rows(step):
+    """Device lengths that sum past the caller's rows (n_nodes, the rows of
+    q_lat): the request crossing n_nodes keeps its first nodes, later requests
+    none.  The buffers carry guard rows past n_nodes, so even an unclamped run
+    would stay inside them; the guard rows must come back untouched, and the
+    rows below n_nodes must match the oracle on the clamped requests.  The
+    records equal the host model's word for word."""
+    import ragged_plan_model as RP
+    dt, H, d_c, d_r = "bf16", 8, 512, 64
+    q_lens, prefixes = [17, 33, 20, 9], [300, 1200, 40, 5000]
+    N, G = 40, 24                       # request 1 keeps 23 of its 33 nodes; 2 and 3 none
+    theta = 10000.0
+    print(f"ragged node bound step={step}", flush=True)
+    q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs(q_lens, prefixes, H, d_c, d_r, dt, 3, seed=77)
+    assert q_lat.shape[0] == sum(q_lens) >= N + G
+    ql_full = torch.from_numpy(q_lat[:N + G]).cuda()
+    qr_full = torch.from_numpy(q_rope[:N + G].copy()).cuda()
+    par_full = torch.from_numpy(parent[:N + G]).cuda()
+    out_full = torch.full((N + G, H, d_c), 7.0, dtype=torch.float32, device="cuda")
+    lse_full = torch.full((N + G, H), 7.0, dtype=torch.float32, device="cuda")
+    kr = _cache(k_rope, dt)
+    if step:  # the cache's prefix rows were rotated when written
+        for b, P in enumerate(prefixes):
+            tv.rope_neox_strided(kr[b:b + 1, :P, :], None, theta)
+    k_before = kr.clone()
+    S = c_kv.shape[1]
+    ws_n = tv.load().tv_verify_attn_ragged_workspace_size(len(q_lens), H, max(q_lens), S, d_c, d_r, tv.TV_BF16)
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device="cuda")
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    pl = torch.tensor(prefixes, dtype=torch.int32).cuda()
+    qlt = torch.tensor(q_lens, dtype=torch.int32).cuda()
+    args = (ql_full[:N], qr_full[:N], _cache(c_kv, dt), kr, par_full[:N], pl, qlt, max(q_lens))
+    if step:
+        tv.verify_step_ragged(*args, theta, sm, out=out_full[:N], lse=lse_full[:N], workspace=ws)
+    else:
+        tv.verify_attn_ragged(*args, sm, out=out_full[:N], lse=lse_full[:N], workspace=ws)
+    torch.cuda.synchronize()
+    model = RP.plan(prefixes, q_lens, H, max(q_lens), S, 128, 256, n_nodes=N)
+    assert [r["q_len"] for r in model["req"]] == [17, 23, 0, 0]
+    words = RP.records_words(model)
+    assert ws[:4 * len(words)].view(torch.int32).cpu().numpy().tolist() == words
+    out, lse = out_full.cpu().numpy(), lse_full.cpu().numpy()
+    assert np.all(out[N:] == 7.0) and np.all(lse[N:] == 7.0)
+    assert np.array_equal(qr_full[N:].cpu().numpy(), q_rope[N:N + G])
+    kb, ka = k_before.view(torch.int16).cpu().numpy(), kr.view(torch.int16).cpu().numpy()
+    for b, (qk, P) in enumerate(zip([17, 23, 0, 0], prefixes)):
+        # rows past the kept nodes (and every prefix row) are never rotated
+        assert np.array_equal(ka[b, :P], kb[b, :P]) and np.array_equal(ka[b, P + qk:], kb[b, P + qk:]), b
+    s = 0
+    for b, (q, P) in enumerate(zip([17, 23], prefixes)):
+        kv = P + q
+        if step:
+            ref = O.verify_step(q_lat[None, s:s + q], q_rope[None, s:s + q], c_kv[b:b + 1, :kv],
+                                k_rope[b:b + 1, :kv], parent[None, s:s + q], P, theta, sm, dt)
+            ref_out, ref_lse = ref["out"], ref["lse"]
+        else:
+            ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat[None, s:s + q], "f32"),
+                                             O.as_f64(q_rope[None, s:s + q], "f32"), O.as_f64(c_kv[b:b + 1, :kv], dt),
+                                             O.as_f64(k_rope[b:b + 1, :kv], dt), parent[None, s:s + q], P, sm)
+        e = errors(out[s:s + q], ref_out[0])
+        assert e["max_rel"] <= TOL[dt]["max_rel"], (b, e)
+        assert np.abs(lse[s:s + q] - ref_lse[0]).max() <= 2.0 ** -7, b
+        s += q

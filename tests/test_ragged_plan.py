@@ -19,8 +19,8 @@ def _merge_slots(rec, mb):
     return row0, rows, [slot0 + s for s in range(n)]
 
 
-def check(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=RP.COST_DEFAULT):
-    rec = RP.plan(prefix, q_len, H, max_q, kv_stride, rpb, target, cost)
+def check(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=RP.COST_DEFAULT, n_nodes=None):
+    rec = RP.plan(prefix, q_len, H, max_q, kv_stride, rpb, target, cost, n_nodes=n_nodes)
     bound_units, bound_slots, bound_merges = RP.launch_bounds(len(q_len), H, max_q, rpb, target)
     assert rec["units"] <= bound_units and rec["merges"] <= bound_merges
     covered = {}
@@ -40,8 +40,12 @@ def check(prefix, q_len, H, max_q, kv_stride, rpb, target, cost=RP.COST_DEFAULT)
     q_start = 0
     for b, r in enumerate(rec["req"]):
         q = min(max(q_len[b], 0), max_q)
+        if n_nodes is not None:
+            q = min(q, max(0, n_nodes - q_start))
         assert r["q_len"] == q and r["q_start"] == q_start
         q_start += q
+        if n_nodes is not None:
+            assert q_start <= n_nodes
         assert r["n_blk"] == -(-(q * H) // rpb)
         kv = r["prefix"] + q
         for rb in range(r["n_blk"]):
@@ -132,3 +136,24 @@ def test_plan_uniform_batch_keeps_whole_blocks():
     rec = RP.plan([8192] * 32, [33] * 32, 64, 33, 8225, **MFMA)
     for r in rec["req"]:
         assert r["b_split"] == 1 and r["t_split"] > 1
+
+
+def test_plan_node_bound():
+    """Device lengths that sum past the caller's n_nodes rows: the request
+    crossing the bound keeps its nodes below it, later ones none, and no unit,
+    slot or merged row reaches past n_nodes."""
+    rng = np.random.default_rng(11)
+    for q_len, prefix, H, max_q in _families(rng):
+        kv_stride = max(p + q for p, q in zip(prefix, q_len)) + 3
+        tot = sum(min(max(q, 0), max_q) for q in q_len)
+        for N in (0, 1, tot // 3, tot - 1, tot, tot + 5):
+            for kern in (MFMA, F32, VALU):
+                rec = check(prefix, q_len, H, max_q, kv_stride, n_nodes=N, **kern)
+                assert sum(r["q_len"] for r in rec["req"]) == min(N, tot)
+                for mb in range(rec["merges"]):
+                    _, _, row0, rows = RP.merge_table(rec)[mb]
+                    assert row0 + rows <= N * H
+    # the crossing request is cut inside itself
+    rec = RP.plan([10, 10, 10], [5, 5, 5], 4, 8, 40, n_nodes=7, **MFMA)
+    assert [r["q_len"] for r in rec["req"]] == [5, 2, 0]
+    assert [r["q_start"] for r in rec["req"]] == [0, 5, 7]

@@ -299,11 +299,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kt + 8 * (i >> 2) + 4 * g2 + (i & 3);
-        const int rel = key - P;  // tree node of a tree key
-        const bool v = key < w.k_end &&
-                       (key < P || (static_cast<unsigned>(rel) < static_cast<unsigned>(w.q_len) &&
-                                    anc_bit(s_anc, node, rel)));
-        m |= static_cast<uint32_t>(v) << i;
+        m |= key_visible(s_anc, node, key, P, w.k_end) << i;
       }
       s_vis[j * kMfmaThreads + threadIdx.x] = static_cast<uint16_t>(m);
     }

@@ -196,21 +196,12 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
       }
       // Mask: keys past the range end, and tree keys that are not ancestors of
       // the row's node (only tiles reaching the tree keys or the range end).
-      // Straight-line on purpose: every lane reads an ancestor word (at a
-      // clamped index) and the visibility is built with integer and/or, then
-      // one select per score.  (Written with short-circuit tests, the device
-      // compiler emitted code that dropped a visible tree key in score
-      // register 0.)
+      // key_visible is straight-line; one select per score.
       if (kt + kF32Keys > min(P, w.k_end)) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int key = kt + 16 * (i >> 2) + 4 * lg + (i & 3);
-          const int rel = min(max(key - P, 0), kMaxQ - 1);
-          const unsigned long long word = s_anc[node * kAncWords + (rel >> 6)];
-          const unsigned in_range = key < w.k_end ? 1u : 0u;
-          const unsigned in_prefix = key < P ? 1u : 0u;
-          const unsigned anc = static_cast<unsigned>((word >> (rel & 63)) & 1ull);
-          p[i] = (in_range & (in_prefix | anc)) != 0u ? p[i] : -INFINITY;
+          p[i] = key_visible(s_anc, node, key, P, w.k_end) != 0u ? p[i] : -INFINITY;
         }
       }
       float tmax = p[0];

@@ -157,16 +157,16 @@ namespace {
 static_assert(kMfmaKeys == kPlanTile && kValuKeys == kPlanTile && kF32Keys == kPlanTile,
               "plans count tiles of 32 keys for every kernel");
 
-// Lengths of request b clamped into the bounds (q_len to [0, max_q], prefix
-// to [0, kv_stride - q_len]); its row blocks and tiles.
+// Lengths of request b as the prep kernel clamped them (into the bounds and
+// the caller's packed node rows) and wrote them into its record; its row
+// blocks and tiles.
 struct ReqLen {
   int q, P, nblk, tiles;
 };
-__device__ __forceinline__ ReqLen req_len(const int32_t* prefix_len, const int32_t* q_len, int b, int H, int max_q,
-                                          int kv_stride, int rpb) {
+__device__ __forceinline__ ReqLen req_len(const int32_t* rq, int b, int H, int rpb) {
   ReqLen r;
-  r.q = min(max(q_len[b], 0), max_q);
-  r.P = min(max(prefix_len[b], 0), kv_stride - r.q);
+  r.q = rq[b * kReqFields + kReqQLen];
+  r.P = rq[b * kReqFields + kReqPrefix];
   r.nblk = (r.q * H + rpb - 1) / rpb;
   r.tiles = (r.P + r.q + kPlanTile - 1) / kPlanTile;
   return r;
@@ -220,8 +220,9 @@ __device__ int block_scan(int v, int* s_wave, int* total) {
 //     (ties by class id), and numbered in that order; nodes, slots and merged
 //     blocks are numbered request by request.
 __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t* __restrict__ prefix_len,
-                                                                   const int32_t* __restrict__ q_len, int B, int H,
-                                                                   int max_q, int kv_stride, int rpb, int target,
+                                                                   const int32_t* __restrict__ q_len, int n_nodes,
+                                                                   int B, int H, int max_q, int kv_stride, int rpb,
+                                                                   int target,
                                                                    int max_slots, int max_merges, PlanCost cost,
                                                                    int32_t* __restrict__ rq) {
   __shared__ long long s_part[kPrepThreads / 64];
@@ -237,9 +238,28 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   const int per = (B + kPrepThreads - 1) / kPrepThreads;
   const int b0 = min(B, t * per), b1 = min(B, b0 + per);
 
+  // 0. Lengths: q_len into [0, max_q], then the packed nodes into the caller's
+  //    n_nodes rows (the request that crosses n_nodes keeps the nodes below it,
+  //    later requests none), prefix into [0, kv_stride - q].  Every later
+  //    phase reads these from the records.
+  {
+    int n_raw = 0;
+    for (int b = b0; b < b1; ++b) n_raw += min(max(q_len[b], 0), max_q);
+    int tot_raw;
+    int o_raw = block_scan(n_raw, s_scan, &tot_raw);
+    for (int b = b0; b < b1; ++b) {
+      const int q = min(max(q_len[b], 0), max_q);
+      const int qc = min(q, max(0, n_nodes - o_raw));
+      o_raw += q;
+      rq[b * kReqFields + kReqQLen] = qc;
+      rq[b * kReqFields + kReqPrefix] = min(max(prefix_len[b], 0), kv_stride - qc);
+    }
+    __syncthreads();
+  }
+
   long long w0 = 0, wt = 0;
   for (int b = b0; b < b1; ++b) {
-    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    const ReqLen r = req_len(rq, b, H, rpb);
     w0 += static_cast<long long>(r.nblk) * (r.tiles + cost.setup);
     wt += static_cast<long long>(r.nblk) * r.tiles;
   }
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   // One (request, candidate) pair per thread at a time.
   for (int i = t; i < B * kPlanCands; i += kPrepThreads) {
     const int b = i / kPlanCands, c = i - b * kPlanCands;
-    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    const ReqLen r = req_len(rq, b, H, rpb);
     if (r.nblk == 0) continue;
     const ReqCut k = cut_request(r.tiles, s_capb[c], s_capt[c]);
     const int last_b = r.tiles - (k.n_body - 1) * k.c_body, last_t = r.tiles - (k.n_tail - 1) * k.c_tail;
@@ -325,7 +345,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   // Per request: nodes, slots, merged blocks (request order).
   int n_q = 0, n_slot = 0, n_merge = 0;
   for (int b = b0; b < b1; ++b) {
-    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    const ReqLen r = req_len(rq, b, H, rpb);
     if (r.nblk == 0) continue;
     const ReqCut k = cut_request(r.tiles, cap_b, cap_t);
     n_q += r.q;
@@ -337,7 +357,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   int o_slot = block_scan(n_slot, s_scan, &tot_slot);
   int o_merge = block_scan(n_merge, s_scan, &tot_merge);
   for (int b = b0; b < b1; ++b) {
-    const ReqLen r = req_len(prefix_len, q_len, b, H, max_q, kv_stride, rpb);
+    const ReqLen r = req_len(rq, b, H, rpb);
     ReqCut k{1, r.tiles, 1, r.tiles};
     if (r.nblk > 0) k = cut_request(r.tiles, cap_b, cap_t);
     int32_t* o = rq + b * kReqFields;
@@ -371,7 +391,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   const int n_cls = 2 * B;
   const bool sorted = n_cls <= kSortMax;
   auto cls_of = [&](int id, int& units, int& len) {
-    const ReqLen r = req_len(prefix_len, q_len, id >> 1, H, max_q, kv_stride, rpb);
+    const ReqLen r = req_len(rq, id >> 1, H, rpb);
     units = 0;
     len = 0;
     if (r.nblk == 0) return;
@@ -633,7 +653,7 @@ hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const Attn
 
 hipError_t launch_ragged_prep(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, const int32_t* prefix_len,
                               const int32_t* q_len, hipStream_t stream) {
-  ragged_prep_kernel<<<dim3(1), kPrepThreads, 0, stream>>>(prefix_len, q_len, s.B, s.H, s.q_len, s.kv_len,
+  ragged_prep_kernel<<<dim3(1), kPrepThreads, 0, stream>>>(prefix_len, q_len, a.n_nodes, s.B, s.H, s.q_len, s.kv_len,
                                                            plan.rows_per_block, static_cast<int>(plan.target),
                                                            static_cast<int>(plan.n_slots),
                                                            static_cast<int>(plan.merge_blocks), plan.kernel == AttnKernel::kMfmaF32 ? kPlanCostF32

@@ -131,9 +131,8 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
     }
     const int key0 = kt + sl;
     const int key1 = kt + sl + 16;
-    // key < k_end <= prefix + q_len, so a tree key's index is below q_len.
-    const bool vis0 = key0 < k_end && (key0 < P || anc_bit(s_anc, node, key0 - P));
-    const bool vis1 = key1 < k_end && (key1 < P || anc_bit(s_anc, node, key1 - P));
+    const bool vis0 = key_visible(s_anc, node, key0, P, k_end) != 0u;
+    const bool vis1 = key_visible(s_anc, node, key1, P, k_end) != 0u;
     const float s0 = vis0 ? acc0 * a.sm_scale : -INFINITY;
     const float s1 = vis1 ? acc1 * a.sm_scale : -INFINITY;
 

@@ -31,25 +31,26 @@ __device__ __forceinline__ void rotate_pair_f64(double x1, double x2, double ang
 
 template <typename T>
 __global__ __launch_bounds__(256) void rope_neox_kernel(typename T::storage* __restrict__ x,
-                                                        const int32_t* __restrict__ pos, int n_tok, int n_head,
+                                                        const int32_t* __restrict__ pos, int64_t n_tok, int n_head,
                                                         int half, int64_t seq_stride, int64_t tok_stride,
                                                         int64_t pos_seq_stride, int64_t total, RopeFreq f) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int k = static_cast<int>(idx % half);
-  int64_t rest = idx / half;
-  const int h = static_cast<int>(rest % n_head);
-  rest /= n_head;
-  const int t = static_cast<int>(rest % n_tok);
-  const int64_t s = rest / n_tok;
-  const int p = pos ? pos[s * pos_seq_stride + t] : t;
-  typename T::storage* row = x + s * seq_stride + static_cast<int64_t>(t) * tok_stride + static_cast<int64_t>(h) * 2 * half;
-  const double x1 = load_f64<T>(row + k);
-  const double x2 = load_f64<T>(row + k + half);
-  double y1, y2;
-  rotate_pair_f64(x1, x2, static_cast<double>(p) * f.inv_freq[k], y1, y2);
-  store_from_f64<T>(row + k, y1);
-  store_from_f64<T>(row + k + half, y2);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int k = static_cast<int>(idx % half);
+    int64_t rest = idx / half;
+    const int h = static_cast<int>(rest % n_head);
+    rest /= n_head;
+    const int64_t t = rest % n_tok;
+    const int64_t s = rest / n_tok;
+    const int64_t p = pos ? pos[s * pos_seq_stride + t] : t;
+    typename T::storage* row = x + s * seq_stride + t * tok_stride + static_cast<int64_t>(h) * 2 * half;
+    const double x1 = load_f64<T>(row + k);
+    const double x2 = load_f64<T>(row + k + half);
+    double y1, y2;
+    rotate_pair_f64(x1, x2, static_cast<double>(p) * f.inv_freq[k], y1, y2);
+    store_from_f64<T>(row + k, y1);
+    store_from_f64<T>(row + k + half, y2);
+  }
 }
 
 // Depth of every node of one tree, into LDS: thread i walks i -> parent -> ...
@@ -147,14 +148,16 @@ __global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_ro
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_rope_neox(void* x, bool bf16, const int32_t* pos, int n_seq, int n_tok, int n_head, int d_r,
+hipError_t launch_rope_neox(void* x, bool bf16, const int32_t* pos, int n_seq, int64_t n_tok, int n_head, int d_r,
                             int64_t seq_stride, int64_t tok_stride, int64_t pos_seq_stride, const RopeFreq& f,
                             hipStream_t stream) {
   const int half = d_r / 2;
   const int64_t total = static_cast<int64_t>(n_seq) * n_tok * n_head * half;
   if (total == 0) return hipSuccess;
   const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
+  // One pair per thread up to 2^20 workgroups; the grid strides past that.
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > (int64_t{1} << 20)) blocks = int64_t{1} << 20;
   if (bf16)
     rope_neox_kernel<BF16><<<dim3(static_cast<unsigned>(blocks)), threads, 0, stream>>>(
         static_cast<uint16_t*>(x), pos, n_tok, n_head, half, seq_stride, tok_stride, pos_seq_stride, total, f);

@@ -9,6 +9,9 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Most rotated pairs one RoPE launch takes (its grid strides over them).
+constexpr int64_t kMaxRopePairs = int64_t{1} << 40;
+
 bool supported_attn(int32_t d_c, int32_t d_r, tv_dtype_t dt) {
   const bool dc_ok = d_c == 64 || d_c == 128 || d_c == 256 || d_c == 512;
   const bool dr_ok = d_r == 32 || d_r == 64;
@@ -99,12 +102,15 @@ tv_status_t plan_ragged(int32_t B, int32_t H, int32_t max_q_len, int32_t kv_stri
 // Checks and kernel arguments of a ragged call (tv_verify_attn_ragged,
 // tv_verify_step_ragged).
 tv_status_t ragged_args(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
-                        const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B, int32_t H,
+                        const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t n_nodes,
+                        int32_t B, int32_t H,
                         int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype,
                         float sm_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
                         tv::AttnShape& s, tv::AttnPlan& plan, tv::AttnArgs& a) {
   const tv_status_t st = plan_ragged(B, H, max_q_len, kv_stride, d_c, d_r, kv_dtype, s, plan);
   if (st != TV_OK) return st;
+  if (n_nodes < 0) return TV_ERR_INVALID;
+  if (static_cast<int64_t>(n_nodes) * H > INT32_MAX) return TV_ERR_UNSUPPORTED;
   if (!q_lat || !q_rope || !c_kv || !k_rope || !parent || !prefix_len || !q_len || !out) return TV_ERR_INVALID;
   if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(parent) & 3u) || (reinterpret_cast<uintptr_t>(prefix_len) & 3u) ||
@@ -141,6 +147,7 @@ tv_status_t ragged_args(const float* q_lat, const float* q_rope, const void* c_k
   a.chunk_tail = plan.chunk_tail;
   a.sm_scale = sm_scale;
   a.kv_stride = kv_stride;
+  a.n_nodes = n_nodes;
   return TV_OK;
 }
 
@@ -157,14 +164,15 @@ size_t tv_verify_attn_ragged_workspace_size(int32_t B, int32_t H, int32_t max_q_
 }
 
 tv_status_t tv_verify_attn_ragged(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
-                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len,
+                                  int32_t n_nodes, int32_t B,
                                   int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
                                   tv_dtype_t kv_dtype, float sm_scale, float* out, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
   tv::AttnShape s;
   tv::AttnPlan plan;
   tv::AttnArgs a;
-  const tv_status_t st = ragged_args(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, B, H, max_q_len,
+  const tv_status_t st = ragged_args(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, n_nodes, B, H, max_q_len,
                                      kv_stride, d_c, d_r, kv_dtype, sm_scale, out, lse, workspace, workspace_bytes, s,
                                      plan, a);
   if (st != TV_OK) return st;
@@ -173,7 +181,8 @@ tv_status_t tv_verify_attn_ragged(const float* q_lat, const float* q_rope, const
 }
 
 tv_status_t tv_verify_step_ragged(const float* q_lat, float* q_rope, const void* c_kv, void* k_rope,
-                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len, int32_t B,
+                                  const int32_t* parent, const int32_t* prefix_len, const int32_t* q_len,
+                                  int32_t n_nodes, int32_t B,
                                   int32_t H, int32_t max_q_len, int32_t kv_stride, int32_t d_c, int32_t d_r,
                                   tv_dtype_t kv_dtype, double theta, float sm_scale, float* out, float* lse,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -182,7 +191,7 @@ tv_status_t tv_verify_step_ragged(const float* q_lat, float* q_rope, const void*
   tv::AttnShape s;
   tv::AttnPlan plan;
   tv::AttnArgs a;
-  const tv_status_t st = ragged_args(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, B, H, max_q_len,
+  const tv_status_t st = ragged_args(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, n_nodes, B, H, max_q_len,
                                      kv_stride, d_c, d_r, kv_dtype, sm_scale, out, lse, workspace, workspace_bytes, s,
                                      plan, a);
   if (st != TV_OK) return st;
@@ -213,9 +222,9 @@ tv_status_t tv_tree_positions(const int32_t* parent, int32_t B, int32_t q_len, i
                                                                                             : TV_ERR_LAUNCH;
 }
 
-tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t n_seq, int32_t n_tok,
-                         int32_t n_head, int32_t d_r, int64_t seq_stride, int64_t tok_stride,
-                         int64_t pos_seq_stride, double theta, hipStream_t stream) {
+tv_status_t tv_rope_neox_strided(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t n_seq, int32_t n_tok,
+                                 int32_t n_head, int32_t d_r, int64_t seq_stride, int64_t tok_stride,
+                                 int64_t pos_seq_stride, double theta, hipStream_t stream) {
   if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID;
   if (n_seq < 0 || n_tok < 0 || n_head < 1 || d_r < 2 || (d_r & 1)) return TV_ERR_INVALID;
   if (d_r > 2 * tv::kMaxHalf) return TV_ERR_UNSUPPORTED;
@@ -223,9 +232,28 @@ tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int32_t 
   if (n_seq == 0 || n_tok == 0) return TV_OK;
   if (!x || seq_stride < 0 || tok_stride < 0 || pos_seq_stride < 0) return TV_ERR_INVALID;
   if (!aligned16(x) || (pos && (reinterpret_cast<uintptr_t>(pos) & 3u))) return TV_ERR_INVALID;
+  if (static_cast<int64_t>(n_seq) * n_tok * n_head * (d_r / 2) > kMaxRopePairs) return TV_ERR_UNSUPPORTED;
   const tv::RopeFreq f = make_freq(d_r, theta);
   return tv::launch_rope_neox(x, dtype == TV_BF16, pos, n_seq, n_tok, n_head, d_r, seq_stride, tok_stride,
                               pos_seq_stride, f, stream) == hipSuccess
+             ? TV_OK
+             : TV_ERR_LAUNCH;
+}
+
+tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int64_t n_tok, int32_t n_head,
+                         int32_t d_r, int64_t tok_stride, double theta, hipStream_t stream) {
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID;
+  if (n_tok < 0 || n_head < 1 || d_r < 2 || (d_r & 1)) return TV_ERR_INVALID;
+  if (d_r > 2 * tv::kMaxHalf) return TV_ERR_UNSUPPORTED;
+  if (!(theta > 0.0) || !isfinite(theta)) return TV_ERR_INVALID;
+  if (n_tok == 0) return TV_OK;
+  if (!x || tok_stride < 0) return TV_ERR_INVALID;
+  if (!aligned16(x) || (pos && (reinterpret_cast<uintptr_t>(pos) & 3u))) return TV_ERR_INVALID;
+  if (n_tok > kMaxRopePairs / (static_cast<int64_t>(n_head) * (d_r / 2))) return TV_ERR_UNSUPPORTED;
+  const tv::RopeFreq f = make_freq(d_r, theta);
+  // One sequence of n_tok tokens.
+  return tv::launch_rope_neox(x, dtype == TV_BF16, pos, 1, n_tok, n_head, d_r, 0, tok_stride, 0, f, stream) ==
+                 hipSuccess
              ? TV_OK
              : TV_ERR_LAUNCH;
 }

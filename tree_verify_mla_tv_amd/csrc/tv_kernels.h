@@ -19,7 +19,7 @@ struct RopeFreq {
   double inv_freq[kMaxHalf];
 };
 
-hipError_t launch_rope_neox(void* x, bool bf16, const int32_t* pos, int n_seq, int n_tok, int n_head, int d_r,
+hipError_t launch_rope_neox(void* x, bool bf16, const int32_t* pos, int n_seq, int64_t n_tok, int n_head, int d_r,
                             int64_t seq_stride, int64_t tok_stride, int64_t pos_seq_stride, const RopeFreq& f,
                             hipStream_t stream);
 hipError_t launch_tree_positions(const int32_t* parent, int B, int q_len, int prefix_len, int32_t* pos,
@@ -109,6 +109,7 @@ struct AttnArgs {
   const int32_t* req;
   const int4* merge_tab;  // the merge table after the records (MergeField order)
   int kv_stride;          // cache rows per request
+  int n_nodes;            // rows of the caller's packed node arrays (the prep clamps the lengths to them)
 };
 
 // Records of a ragged batch, written by the prep kernel into the workspace
@@ -443,6 +444,23 @@ __device__ __forceinline__ void build_ancestors(const int32_t* __restrict__ pare
 // Whether tree key rel (0 <= rel < q_len) is visible from node `node`.
 __device__ __forceinline__ bool anc_bit(const unsigned long long* s_anc, int node, int rel) {
   return ((s_anc[node * kAncWords + (rel >> 6)] >> (rel & 63)) & 1ull) != 0ull;
+}
+
+// 1 if kv key `key` is visible from tree node `node` (0 <= node < kMaxQ): the
+// key lies below the unit's range end k_end and is a prefix key (key < P) or
+// the node or one of its ancestors.  Written straight-line on purpose: every
+// lane reads an ancestor word at a clamped index and the answer is built with
+// integer and/or, with no short-circuit test.  (With the form
+// `key < k_end && (key < P || anc_bit(...))` the device compiler once emitted
+// code that dropped a visible tree key.)
+__device__ __forceinline__ unsigned key_visible(const unsigned long long* s_anc, int node, int key, int P,
+                                                int k_end) {
+  const int rel = min(max(key - P, 0), kMaxQ - 1);
+  const unsigned long long word = s_anc[node * kAncWords + (rel >> 6)];
+  const unsigned in_range = key < k_end ? 1u : 0u;
+  const unsigned in_prefix = key < P ? 1u : 0u;
+  const unsigned anc = static_cast<unsigned>((word >> (rel & 63)) & 1ull);
+  return in_range & (in_prefix | anc);
 }
 
 }  // namespace tv

@@ -33,7 +33,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "tv_status_str": (ctypes.c_char_p, [_i32]),
     "tv_tree_positions": (_i32, [_p, _i32, _i32, _i32, _p, _p]),
-    "tv_rope_neox": (_i32, [_p, _i32, _p, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _f64, _p]),
+    "tv_rope_neox": (_i32, [_p, _i32, _p, _i64, _i32, _i32, _i64, _f64, _p]),
+    "tv_rope_neox_strided": (_i32, [_p, _i32, _p, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _f64, _p]),
     "tv_verify_attn": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
                               _sz, _p]),
     "tv_verify_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
@@ -44,11 +45,11 @@ SIGNATURES = {
     "tv_tree_accept": (_i32, [_p, _p, _p, _i32, _i32, _p, _p, _p, _p]),
     "tv_kv_compact": (_i32, [_p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]),
     "tv_tree_build": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
-    "tv_verify_attn_ragged": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                                     _p, _p, _p, _sz, _p]),
-    "tv_verify_attn_ragged_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
-    "tv_verify_step_ragged": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f64,
+    "tv_verify_attn_ragged": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _f32, _p, _p, _p, _sz, _p]),
+    "tv_verify_attn_ragged_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "tv_verify_step_ragged": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _f64, _f32, _p, _p, _p, _sz, _p]),
 }
 
 
@@ -120,7 +121,32 @@ def tree_positions(parent: torch.Tensor, prefix_len: int, out: torch.Tensor | No
 
 
 def rope_neox(x: torch.Tensor, pos: torch.Tensor | None = None, theta: float = 10000.0) -> torch.Tensor:
-    """In-place NeoX RoPE (float64 angles) of x [n_seq, n_tok, (n_head,) d_r].
+    """In-place NeoX RoPE (float64 angles) of x [n_tok, (n_head,) d_r]: tv_rope_neox.
+
+    The head and feature axes must be dense; the token axis may be strided.
+    pos: int32 [n_tok] contiguous, or None for position = token index.
+    """
+    _need(x.is_cuda, "x must be a CUDA tensor")
+    if x.dim() == 2:
+        n_tok, d_r = x.shape
+        n_head = 1
+    else:
+        _need(x.dim() == 3, "x must be [n_tok, n_head, d_r] or [n_tok, d_r]")
+        n_tok, n_head, d_r = x.shape
+        _need(n_head == 1 or x.stride(1) == d_r, "heads of x must be dense rows")
+    _need(x.stride(-1) == 1, "the feature axis of x must be contiguous")
+    dt = _kv_dtype(x)
+    if pos is not None:
+        _need(pos.is_cuda and pos.dtype == torch.int32 and pos.shape == (n_tok,) and pos.is_contiguous(),
+              "pos must be contiguous CUDA int32 [n_tok]")
+    _check("tv_rope_neox", load().tv_rope_neox(_ptr(x), dt, _ptr(pos), n_tok, n_head, d_r, x.stride(0),
+                                               float(theta), _stream()))
+    return x
+
+
+def rope_neox_strided(x: torch.Tensor, pos: torch.Tensor | None = None, theta: float = 10000.0) -> torch.Tensor:
+    """In-place NeoX RoPE (float64 angles) of x [n_seq, n_tok, (n_head,) d_r]:
+    tv_rope_neox_strided.
 
     The head and feature axes must be dense; the sequence and token axes may be
     strided (e.g. a slice of a kv cache).  pos: int32 [n_seq, n_tok] (row stride
@@ -141,8 +167,9 @@ def rope_neox(x: torch.Tensor, pos: torch.Tensor | None = None, theta: float = 1
         _need(pos.is_cuda and pos.dtype == torch.int32 and pos.shape == (n_seq, n_tok) and pos.stride(1) == 1,
               "pos must be CUDA int32 [n_seq, n_tok] with unit token stride")
         pos_stride = pos.stride(0)
-    _check("tv_rope_neox", load().tv_rope_neox(_ptr(x), dt, _ptr(pos), n_seq, n_tok, n_head, d_r, x.stride(0),
-                                               x.stride(1), pos_stride, float(theta), _stream()))
+    _check("tv_rope_neox_strided", load().tv_rope_neox_strided(_ptr(x), dt, _ptr(pos), n_seq, n_tok, n_head, d_r,
+                                                               x.stride(0), x.stride(1), pos_stride, float(theta),
+                                                               _stream()))
     return x
 
 
@@ -212,7 +239,9 @@ def verify_attn_ragged(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, m
     q_rope [N, H, d_r], parent [N] int32 (local node indices); cache c_kv
     [B, kv_stride, d_c], k_rope [B, kv_stride, d_r]; prefix_len and q_len: int32
     [B] device tensors (q_len[b] <= max_q_len, prefix_len[b] + q_len[b] <=
-    kv_stride, N >= sum of q_len).  Returns out [N, H, d_c] (and lse [N, H])."""
+    kv_stride).  N (the rows of q_lat) bounds the packed nodes: if the lengths
+    sum to more, the request crossing N keeps its nodes below N and later
+    requests get none.  Returns out [N, H, d_c] (and lse [N, H])."""
     return _ragged("tv_verify_attn_ragged", q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, max_q_len,
                    sm_scale, out, lse, return_lse, workspace, None)
 
@@ -240,13 +269,18 @@ def _ragged(fn, q_lat, q_rope, c_kv, k_rope, parent, prefix_len, q_len, max_q_le
     _need(ws_bytes > 0, "unsupported shape for the ragged attention")
     if out is None:
         out = torch.empty_like(q_lat)
+    _cuda_contig("out", out)
+    _need(out.dtype == torch.float32 and out.shape == (N, H, d_c), "out must be float32 [N, H, d_c]")
     if lse is None and return_lse:
         lse = torch.empty(N, H, dtype=torch.float32, device=q_lat.device)
+    if lse is not None:
+        _cuda_contig("lse", lse)
+        _need(lse.dtype == torch.float32 and lse.shape == (N, H), "lse must be float32 [N, H]")
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q_lat.device)
     ws_n = workspace.numel() * workspace.element_size()
-    head = (_ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), _ptr(prefix_len), _ptr(q_len), B, H,
-            max_q_len, S, d_c, d_r, dt)
+    head = (_ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), _ptr(prefix_len), _ptr(q_len), N, B,
+            H, max_q_len, S, d_c, d_r, dt)
     tail = (float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_n, _stream())
     args = head + tail if theta is None else head + (float(theta),) + tail
     _check(fn, getattr(load(), fn)(*args))
