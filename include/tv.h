@@ -148,6 +148,26 @@ tv_status_t tv_verify_attn(const float* q_lat, const float* q_rope, const void* 
                            int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
                            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * tv_verify_attn_noalloc — tv_verify_attn with no workspace argument, for
+ *   callers that cannot allocate device memory (code under HIP graph capture,
+ *   tight serving loops, harnesses that forbid allocation).  It allocates
+ *   nothing: the split-kv partial results go to a static device array of
+ *   TV_NOALLOC_SCRATCH_BYTES in the library (one per device, held until the
+ *   process ends; its address is looked up on a device's first call).
+ *   Arguments, results and kernels are those of tv_verify_attn.
+ *   Shapes whose tv_verify_attn_workspace_size exceeds TV_NOALLOC_SCRATCH_BYTES
+ *   return TV_ERR_UNSUPPORTED before anything else happens.  Every call on a
+ *   device shares that device's array (nothing in it needs to start at zero):
+ *   calls that overlap on one device -- on different streams or threads --
+ *   race and give wrong results; serialise them.
+ */
+#define TV_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+tv_status_t tv_verify_attn_noalloc(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                                   const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                                   int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
+                                   float* lse, hipStream_t stream);
+
 /* Bytes of workspace tv_verify_attn / tv_verify_step need for these shapes
  * (split-kv partial results); 0 when the launch needs none.  Depends on the
  * shapes only, never on the device. */

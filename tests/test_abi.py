@@ -238,3 +238,26 @@ def test_verify_attn_ragged_rejects_before_launch():
     assert call(d_c=100) == UNS
     assert call(N=-1) == INV                              # negative node count
     assert call(N=2**28) == UNS                           # N * H rows past int32
+
+
+def test_verify_attn_noalloc_rejects_before_launch():
+    """The no-allocation entry point checks its arguments like tv_verify_attn,
+    and a shape whose split-kv scratch exceeds the static array is refused
+    before any device call."""
+    lib = tv.load()
+    f = lib.tv_verify_attn_noalloc
+
+    def call(prefix=4, B=1, H=2, q=3, d_c=64, d_r=32, dt=0, out=A, q_lat=A):
+        return f(q_lat, A, A, A, A, prefix, B, H, q, d_c, d_r, dt, 0.1, out, None, None)
+
+    assert call(out=None) == INV
+    assert call(q_lat=A + 8) == INV
+    assert call(B=0) == INV
+    assert call(q=257) == UNS
+    assert call(d_c=100) == UNS
+    # four long trees: every row block cut into many kv pieces, ~268 MB of partials
+    need = tv.workspace_size(4, 64, 33, 200000, 512, 64, tv.TV_BF16)
+    assert need > tv.TV_NOALLOC_SCRATCH_BYTES
+    assert call(prefix=200000, B=4, H=64, q=33, d_c=512, d_r=64, dt=1) == UNS
+    # the serving batch fits the array
+    assert 0 < tv.workspace_size(32, 64, 33, 8192, 512, 64, tv.TV_BF16) <= tv.TV_NOALLOC_SCRATCH_BYTES

@@ -2,10 +2,39 @@
 // planning and kernel dispatch.  Nothing here allocates or synchronises.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tv.h"
 #include "tv_kernels.h"
 
+// Split-kv scratch of tv_verify_attn_noalloc: one copy per device, held until
+// the process ends.  Host code never passes this name to a kernel (on the host
+// it is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[TV_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -277,6 +306,28 @@ tv_status_t tv_verify_attn(const float* q_lat, const float* q_rope, const void* 
   if (!isfinite(sm_scale)) return TV_ERR_INVALID;
   return run_attention(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, B, H, q_len, d_c, d_r, kv_dtype, sm_scale,
                        out, lse, workspace, workspace_bytes, stream);
+}
+
+tv_status_t tv_verify_attn_noalloc(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                                   const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                                   int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
+                                   float* lse, hipStream_t stream) {
+  const tv_status_t st = check_attn_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype);
+  if (st != TV_OK) return st;
+  if (!q_lat || !q_rope || !c_kv || !k_rope || !parent || !out) return TV_ERR_INVALID;
+  if (!aligned16(q_lat) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(parent) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return TV_ERR_INVALID;
+  if (!isfinite(sm_scale)) return TV_ERR_INVALID;
+  const size_t need = tv::plan_attention(make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype)).ws_bytes;
+  if (need > TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_on_current_device();
+    if (!ws) return TV_ERR_LAUNCH;
+  }
+  return run_attention(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, B, H, q_len, d_c, d_r, kv_dtype, sm_scale,
+                       out, lse, ws, TV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 tv_status_t tv_tree_rope(float* q_rope, void* k_rope, tv_dtype_t kv_dtype, const int32_t* parent,

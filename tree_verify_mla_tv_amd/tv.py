@@ -20,6 +20,7 @@ TV_F32, TV_BF16 = 0, 1
 TV_MAX_Q_LEN = 256
 TV_MAX_BUILD_BUDGET = TV_MAX_Q_LEN - 1
 TV_MAX_BUILD_CANDIDATES = 8192
+TV_NOALLOC_SCRATCH_BYTES = 80 << 20
 
 _lib = None
 
@@ -38,6 +39,8 @@ SIGNATURES = {
     "tv_verify_attn": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
                               _sz, _p]),
     "tv_verify_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "tv_verify_attn_noalloc": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p,
+                                      _p]),
     "tv_tree_rope": (_i32, [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f64, _p]),
     "tv_verify_step": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f64, _f32, _p, _p,
                               _p, _sz, _p]),
@@ -229,6 +232,23 @@ def verify_attn(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, sm_scale: 
     _check("tv_verify_attn", load().tv_verify_attn(
         _ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
         float(sm_scale), _ptr(out), _ptr(lse_t), _ptr(workspace), ws_n, _stream()))
+    return (out, lse_t) if (return_lse or lse is not None) else out
+
+
+def verify_attn_noalloc(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, sm_scale: float | None = None,
+                        out=None, lse=None, return_lse: bool = False):
+    """verify_attn through tv_verify_attn_noalloc: the split-kv scratch is the
+    library's static device array (no workspace).  out / lse must be given for
+    a call that may not allocate; when they are None they are allocated here,
+    before the library call."""
+    B, q, H, d_c, d_r = _attn_shapes(q_lat, q_rope, c_kv, k_rope, parent, prefix_len)
+    dt = _kv_dtype(c_kv)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d_c + d_r)
+    out, lse_t, _ = _outputs(q_lat, out, lse, return_lse, None, 0)
+    _check("tv_verify_attn_noalloc", load().tv_verify_attn_noalloc(
+        _ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
+        float(sm_scale), _ptr(out), _ptr(lse_t), _stream()))
     return (out, lse_t) if (return_lse or lse is not None) else out
 
 
