@@ -36,10 +36,18 @@ PEAKS_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32_mfma": 157.3, "f32_valu": 15
 # Which kernel the library runs for each cache dtype, the arithmetic it does,
 # and the roofline that bounds it.
 KERNELS = {
-    "bf16": dict(name="attn_mfma_bf16_kernel",
-                 source=["tree_verify_mla_tv_amd/csrc/attn_mfma.hip", "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h",
+    "bf16": dict(name="attn_mfma_q2_kernel",
+                 source=["tree_verify_mla_tv_amd/csrc/attn_mfma_q2.hip", "tree_verify_mla_tv_amd/csrc/attn_mfma_q2_asm.h",
+                         "tree_verify_mla_tv_amd/csrc/attn_mfma_common.h", "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h",
                          "tree_verify_mla_tv_amd/csrc/tv_kernels.h"],
                  bound="mfma", peak="bf16", dtype="bf16"),
+    # tv_verify_attn_ex with TV_ATTN_BF16_QUERIES: the queries rounded to one bf16 term
+    "bf16_queries": dict(name="attn_mfma_bf16_kernel",
+                         source=["tree_verify_mla_tv_amd/csrc/attn_mfma.hip",
+                                 "tree_verify_mla_tv_amd/csrc/attn_mfma_common.h",
+                                 "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h",
+                                 "tree_verify_mla_tv_amd/csrc/tv_kernels.h"],
+                         bound="mfma", peak="bf16", dtype="bf16"),
     "f32": dict(name="attn_mfma_f32_kernel", source=["tree_verify_mla_tv_amd/csrc/attn_mfma_f32.hip",
                                                     "tree_verify_mla_tv_amd/csrc/tv_kernels.h"], bound="mfma",
                 peak="f32_mfma", dtype="f32"),

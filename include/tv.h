@@ -134,11 +134,13 @@ tv_status_t tv_rope_neox_strided(void* x, tv_dtype_t dtype, const int32_t* pos, 
  *   latent rows (kv_len * d_c elements of kv_dtype) must stay below 2^31
  *   bytes (TV_ERR_UNSUPPORTED otherwise).
  *   Arithmetic: with a bf16 cache at (512, 64) both contractions run on bf16
- *   matrix cores (the scaled queries and the softmax weights rounded to bf16,
- *   fp32 accumulation and row sums); with an fp32 cache at (512, 64) on fp32
- *   matrix cores; other shapes on the fp32 vector ALU.  The sums run in a
- *   different order than the plain definition; the results agree with it to
- *   fp32 (or, for the bf16 path, bf16-operand) rounding.
+ *   matrix cores: each scaled query x = sm_scale * log2(e) * q (rounded to
+ *   fp32) enters as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi), so
+ *   the scores are those of the fp32 queries to fp32 accumulation; the
+ *   softmax weights are rounded to bf16 for the value product (fp32
+ *   accumulation, row sums of the rounded weights).  With an fp32 cache at
+ *   (512, 64) on fp32 matrix cores; other shapes on the fp32 vector ALU.  The
+ *   sums run in a different order than the plain definition.
  *   workspace: caller-owned device scratch of at least
  *   tv_verify_attn_workspace_size(...) bytes (NULL allowed when that is 0).
  *   out must not overlap any input.
@@ -167,6 +169,26 @@ tv_status_t tv_verify_attn_noalloc(const float* q_lat, const float* q_rope, cons
                                    const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
                                    int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
                                    float* lse, hipStream_t stream);
+
+/*
+ * tv_verify_attn_ex — tv_verify_attn with option flags (0 gives tv_verify_attn
+ *   exactly).  [Verify page, as for tv_verify_attn]
+ *   TV_ATTN_BF16_QUERIES: with a bf16 cache at (512, 64), round each scaled
+ *   query to ONE bf16 term (a single score pass over twice the rows per
+ *   workgroup: faster, but every score moves by up to 2^-9 of its terms;
+ *   right when the queries are bf16 values already, or when that error is
+ *   acceptable).  No effect on other shapes.  Unknown flag bits return
+ *   TV_ERR_INVALID.  The workspace must hold
+ *   tv_verify_attn_ex_workspace_size(..., flags) bytes.
+ */
+#define TV_ATTN_BF16_QUERIES 1u
+tv_status_t tv_verify_attn_ex(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                              const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                              int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, uint32_t flags,
+                              float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes of tv_verify_attn_ex with these flags (0 for bad flags). */
+size_t tv_verify_attn_ex_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_t prefix_len, int32_t d_c,
+                                        int32_t d_r, tv_dtype_t kv_dtype, uint32_t flags);
 
 /* Bytes of workspace tv_verify_attn / tv_verify_step need for these shapes
  * (split-kv partial results); 0 when the launch needs none.  Depends on the

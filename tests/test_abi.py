@@ -261,3 +261,22 @@ def test_verify_attn_noalloc_rejects_before_launch():
     assert call(prefix=200000, B=4, H=64, q=33, d_c=512, d_r=64, dt=1) == UNS
     # the serving batch fits the array
     assert 0 < tv.workspace_size(32, 64, 33, 8192, 512, 64, tv.TV_BF16) <= tv.TV_NOALLOC_SCRATCH_BYTES
+
+
+def test_verify_attn_ex_flags():
+    """tv_verify_attn_ex: flags 0 is tv_verify_attn; TV_ATTN_BF16_QUERIES
+    selects the one-term query kernel (its own workspace size); unknown bits
+    are refused before launch."""
+    lib = tv.load()
+    f = lib.tv_verify_attn_ex
+    assert f(A, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.1, 2, A, None, None, 0, None) == INV     # unknown flag
+    assert f(A, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.1, 1 << 31, A, None, None, 0, None) == INV
+    assert f(None, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.1, 1, A, None, None, 0, None) == INV
+    assert f(A, A, A, A, A, 4, 1, 2, 257, 64, 32, 0, 0.1, 1, A, None, None, 0, None) == UNS
+    ws = lib.tv_verify_attn_ex_workspace_size
+    assert ws(32, 64, 33, 8192, 512, 64, 1, 2) == 0                   # unknown flag
+    # serving batch: 64-row blocks with two-term queries, 128-row blocks with one
+    two, one = ws(32, 64, 33, 8192, 512, 64, 1, 0), ws(32, 64, 33, 8192, 512, 64, 1, 1)
+    assert two == tv.workspace_size(32, 64, 33, 8192, 512, 64, tv.TV_BF16) and 0 < two < one
+    # the flag changes nothing for the fp32 cache
+    assert ws(2, 64, 9, 5000, 512, 64, 0, 1) == ws(2, 64, 9, 5000, 512, 64, 0, 0)

@@ -429,3 +429,42 @@ def test_topological_relabelling_permutes_outputs(kernel):
     ref, _ = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, dt),
                            O.as_f64(k_rope, dt), parent, P, 0.04)
     _check_tol(errors(o1, ref), dt, kernel)
+
+
+# ---------------------------------------------------------------------------
+# The bf16-queries option (tv_verify_attn_ex, TV_ATTN_BF16_QUERIES)
+# ---------------------------------------------------------------------------
+BF16Q_EDGE = [c for c in EDGE if c[4:7] == (512, 64, "bf16")]
+
+
+@pytest.mark.parametrize("case", BF16Q_EDGE, ids=[f"B{c[0]}H{c[1]}q{c[2]}P{c[3]}{c[7]}" for c in BF16Q_EDGE])
+def test_bf16_queries_edge_shapes(case):
+    """The one-term query kernel on the bf16-cache edge shapes, against the
+    oracle at the bf16 bound."""
+    B, H, q, P, d_c, d_r, dt, tree = case
+    q_lat, q_rope, c_kv, k_rope, parent = _edge_inputs(*case, seed=zlib.crc32(str(case).encode()))
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, dt),
+                                     O.as_f64(k_rope, dt), parent, P, sm)
+    out, lse = tv.verify_attn_ex(cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, dt), cuda_cache(k_rope, dt),
+                                 torch.from_numpy(parent).cuda(), P, sm, tv.TV_ATTN_BF16_QUERIES, return_lse=True)
+    torch.cuda.synchronize()
+    check_out("edge bf16 queries", str(case), out, lse, ref_out, ref_lse, dt)
+
+
+def test_bf16_queries_serving_scale():
+    """The serving batch through the one-term query kernel (rotated by the
+    step's RoPE first), every tree against the oracle."""
+    w = W.WORKLOADS[W.SERVING]
+    inp = W.make_inputs(w)
+    ref = O.verify_step(inp["q_lat"], inp["q_rope"], inp["c_kv"], inp["k_rope"], inp["parent"], w.prefix_len,
+                        w.theta, w.sm_scale, w.kv_dtype)
+    q_lat, q_rope = cuda_f32(inp["q_lat"]), cuda_f32(inp["q_rope"])
+    c_kv, k_rope = cuda_cache(inp["c_kv"], "bf16"), cuda_cache(inp["k_rope"], "bf16")
+    parent = torch.from_numpy(inp["parent"]).cuda()
+    tv.rope_neox_strided(k_rope[:, :w.prefix_len, :], None, w.theta)
+    tv.tree_rope(q_rope, k_rope, parent, w.prefix_len, w.theta)
+    out, lse = tv.verify_attn_ex(q_lat, q_rope, c_kv, k_rope, parent, w.prefix_len, w.sm_scale,
+                                 tv.TV_ATTN_BF16_QUERIES, return_lse=True)
+    torch.cuda.synchronize()
+    check_out(w.name + " bf16 queries", w.describe(), out, lse, ref["out"], ref["lse"], "bf16")

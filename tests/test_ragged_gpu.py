@@ -207,7 +207,7 @@ def test_ragged_records_match_plan_model(which):
                                 torch.tensor(q_lens, dtype=torch.int32).cuda(), max_q, sm, workspace=ws)
     torch.cuda.synchronize()
     if d_c == 512 and d_r == 64:  # the matrix-core kernels: rows per workgroup, workgroups at once, costs
-        rpb, target, cost = (128, 256, RP.COST_DEFAULT) if dt == "bf16" else (64, 256, RP.COST_F32)
+        rpb, target, cost = (64, 256, RP.COST_DEFAULT) if dt == "bf16" else (64, 256, RP.COST_F32)
     else:
         rpb, target, cost = 16, 512, RP.COST_DEFAULT
     model = RP.records_words(RP.plan(prefixes, q_lens, H, max_q, S, rpb, target, cost))
@@ -246,7 +246,7 @@ def test_ragged_records_unsorted_large_batch():
                                 torch.tensor(prefixes, dtype=torch.int32).cuda(),
                                 torch.tensor(q_lens, dtype=torch.int32).cuda(), max(q_lens), sm, workspace=ws)
     torch.cuda.synchronize()
-    model = RP.plan(prefixes, q_lens, H, max(q_lens), S, 128, 256)
+    model = RP.plan(prefixes, q_lens, H, max(q_lens), S, 64, 256)
     assert model["cls_id"] == list(range(2 * B))
     words = RP.records_words(model)
     assert ws[:4 * len(words)].view(torch.int32).cpu().numpy().tolist() == words
@@ -300,7 +300,7 @@ def test_ragged_lengths_past_node_rows(step):
     else:
         tv.verify_attn_ragged(*args, sm, out=out_full[:N], lse=lse_full[:N], workspace=ws)
     torch.cuda.synchronize()
-    model = RP.plan(prefixes, q_lens, H, max(q_lens), S, 128, 256, n_nodes=N)
+    model = RP.plan(prefixes, q_lens, H, max(q_lens), S, 64, 256, n_nodes=N)
     assert [r["q_len"] for r in model["req"]] == [17, 23, 0, 0]
     words = RP.records_words(model)
     assert ws[:4 * len(words)].view(torch.int32).cpu().numpy().tolist() == words

@@ -7,7 +7,8 @@ import pytest
 
 import ragged_plan_model as RP
 
-MFMA = dict(rpb=128, target=256)
+MFMA = dict(rpb=128, target=256)      # bf16 cache, one-term queries
+Q2 = dict(rpb=64, target=256)         # bf16 cache, two-term queries (the default)
 F32 = dict(rpb=64, target=256, cost=RP.COST_F32)
 VALU = dict(rpb=16, target=512)
 
@@ -85,7 +86,7 @@ def test_plan_covers_and_bounds(seed):
     rng = np.random.default_rng(seed)
     for q_len, prefix, H, max_q in _families(rng):
         kv_stride = max(p + q for p, q in zip(prefix, q_len)) + 3
-        for kern in (MFMA, F32, VALU):
+        for kern in (MFMA, Q2, F32, VALU):
             check(prefix, q_len, H, max_q, kv_stride, **kern)
 
 
@@ -147,7 +148,7 @@ def test_plan_node_bound():
         kv_stride = max(p + q for p, q in zip(prefix, q_len)) + 3
         tot = sum(min(max(q, 0), max_q) for q in q_len)
         for N in (0, 1, tot // 3, tot - 1, tot, tot + 5):
-            for kern in (MFMA, F32, VALU):
+            for kern in (MFMA, Q2, F32, VALU):
                 rec = check(prefix, q_len, H, max_q, kv_stride, n_nodes=N, **kern)
                 assert sum(r["q_len"] for r in rec["req"]) == min(N, tot)
                 for mb in range(rec["merges"]):

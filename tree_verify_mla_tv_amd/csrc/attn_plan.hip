@@ -60,22 +60,53 @@ void cut_for_blocks(int kv_len, long long blocks, long long slots, int tile, int
 }
 }  // namespace
 
-AttnPlan plan_attention(const AttnShape& s) {
-  AttnPlan p{};
+// Kernel of a shape: the bf16-cache matrix-core kernels at (512, 64) -- the
+// queries as two bf16 terms unless bf16_queries asks for one -- the fp32-cache
+// matrix-core kernel at (512, 64), the vector-ALU kernel otherwise.
+void choose_kernel(const AttnShape& s, AttnPlan& p) {
   const bool mfma = s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
   const bool f32 = !s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
-  p.kernel = mfma ? AttnKernel::kMfmaBf16 : f32 ? AttnKernel::kMfmaF32 : AttnKernel::kValu;
-  p.rows_per_block = mfma ? kMfmaRows : f32 ? kF32Rows : kValuRows;
+  p.kernel = mfma ? (s.bf16_queries ? AttnKernel::kMfmaBf16 : AttnKernel::kMfmaBf16Q2)
+                  : f32 ? AttnKernel::kMfmaF32 : AttnKernel::kValu;
+  p.rows_per_block = p.kernel == AttnKernel::kMfmaBf16   ? kMfmaRows
+                     : p.kernel == AttnKernel::kMfmaBf16Q2 ? kQ2Rows
+                     : f32                                 ? kF32Rows
+                                                           : kValuRows;
   p.keys_per_tile = mfma ? kMfmaKeys : kValuKeys;
+}
+
+AttnPlan plan_attention(const AttnShape& s) {
+  AttnPlan p{};
+  choose_kernel(s, p);
+  const bool mfma = p.kernel == AttnKernel::kMfmaBf16 || p.kernel == AttnKernel::kMfmaBf16Q2;
+  const bool f32 = p.kernel == AttnKernel::kMfmaF32;
   const int R = s.q_len * s.H;
   p.n_rb = ceil_div(R, p.rows_per_block);
-  const bool has_tail = (R % p.rows_per_block) != 0;
-  p.full_rb = has_tail ? p.n_rb - 1 : p.n_rb;
+  bool has_tail = (R % p.rows_per_block) != 0;
   // Workgroups resident per CU: a matrix-core kernel takes a whole CU; the VALU
   // one about one, so aim at two rounds for it.
   const long long target = mfma || f32 ? kNumCU : 2 * kNumCU;
 
   const long long blocks = static_cast<long long>(s.B) * p.n_rb;
+  if (!has_tail && p.n_rb > 1 && blocks > target && blocks % target != 0) {
+    // Whole blocks only, but the last round of workgroups would be partly
+    // idle: treat each tree's last block as the tail to cut into pieces when
+    // that shortens the launch (in rounds of whole-block units; pieces that
+    // fit beside the last round's full units cost nothing, an extra round of
+    // pieces 1 / split; plus a tenth of a round for the merge).
+    const long long full_units = static_cast<long long>(s.B) * (p.n_rb - 1);
+    const long long rem = full_units % target;
+    long long free_slots = target - rem;
+    if (free_slots < s.B) free_slots += target;
+    int n, chunk;
+    cut(s.kv_len, static_cast<int>(free_slots / s.B), p.keys_per_tile, n, chunk,
+        f32 ? kF32MinKeysPerSplit : kMinKeysPerSplit);
+    const bool fits = rem != 0 && static_cast<long long>(s.B) * n <= target - rem;
+    const double t_cut = static_cast<double>((full_units + target - 1) / target) + (fits ? 0.0 : 1.0 / n) + 0.1;
+    const double t_whole = static_cast<double>((blocks + target - 1) / target);
+    if (n > 1 && t_cut < t_whole) has_tail = true;
+  }
+  p.full_rb = has_tail ? p.n_rb - 1 : p.n_rb;
   if (blocks < target) {
     // Too few row blocks: cut every block's kv range.  A unit's set-up (tree
     // masks, queries, first tile, output) costs about ten tile-steps.
@@ -127,11 +158,9 @@ AttnPlan plan_attention(const AttnShape& s) {
 // + slots; merged blocks <= min(B n_rb, slots / 2).
 AttnPlan plan_attention_ragged(const AttnShape& s) {
   AttnPlan p{};
-  const bool mfma = s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
-  const bool f32 = !s.kv_bf16 && s.d_c == 512 && s.d_r == 64;
-  p.kernel = mfma ? AttnKernel::kMfmaBf16 : f32 ? AttnKernel::kMfmaF32 : AttnKernel::kValu;
-  p.rows_per_block = mfma ? kMfmaRows : f32 ? kF32Rows : kValuRows;
-  p.keys_per_tile = mfma ? kMfmaKeys : kValuKeys;
+  choose_kernel(s, p);
+  const bool mfma = p.kernel == AttnKernel::kMfmaBf16 || p.kernel == AttnKernel::kMfmaBf16Q2;
+  const bool f32 = p.kernel == AttnKernel::kMfmaF32;
   p.n_rb = ceil_div(static_cast<long long>(s.q_len) * s.H, p.rows_per_block);
   p.full_rb = p.n_rb;
   p.split_full = p.split_tail = 1;
@@ -626,9 +655,10 @@ __global__ __launch_bounds__(256) void attn_merge_ragged_kernel(AttnArgs a, int 
 }
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  hipError_t e = plan.kernel == AttnKernel::kMfmaBf16  ? launch_attn_mfma_bf16(s, plan, a, stream)
-                 : plan.kernel == AttnKernel::kMfmaF32 ? launch_attn_mfma_f32(s, plan, a, stream)
-                                                       : launch_attn_valu(s, plan, a, stream);
+  hipError_t e = plan.kernel == AttnKernel::kMfmaBf16Q2 ? launch_attn_mfma_q2(s, plan, a, stream)
+                 : plan.kernel == AttnKernel::kMfmaBf16 ? launch_attn_mfma_bf16(s, plan, a, stream)
+                 : plan.kernel == AttnKernel::kMfmaF32  ? launch_attn_mfma_f32(s, plan, a, stream)
+                                                        : launch_attn_valu(s, plan, a, stream);
   if (e != hipSuccess || plan.merge_blocks == 0) return e;
   if (a.req) {
     // The tasks of the bound (merged blocks x tasks per block), at most 8

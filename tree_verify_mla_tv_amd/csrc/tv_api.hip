@@ -38,6 +38,9 @@ void* scratch_on_current_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Flags tv_verify_attn_ex knows.
+constexpr uint32_t kAttnFlags = TV_ATTN_BF16_QUERIES;
+
 // Most rotated pairs one RoPE launch takes (its grid strides over them).
 constexpr int64_t kMaxRopePairs = int64_t{1} << 40;
 
@@ -72,15 +75,16 @@ tv_status_t check_attn_shape(int32_t prefix_len, int32_t B, int32_t H, int32_t q
 }
 
 tv::AttnShape make_shape(int32_t prefix_len, int32_t B, int32_t H, int32_t q_len, int32_t d_c, int32_t d_r,
-                         tv_dtype_t kv_dtype) {
-  return tv::AttnShape{B, H, q_len, prefix_len, prefix_len + q_len, d_c, d_r, kv_dtype == TV_BF16};
+                         tv_dtype_t kv_dtype, uint32_t flags = 0) {
+  return tv::AttnShape{B,   H,   q_len, prefix_len, prefix_len + q_len,
+                       d_c, d_r, kv_dtype == TV_BF16, (flags & TV_ATTN_BF16_QUERIES) != 0};
 }
 
 tv_status_t run_attention(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
                           const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
                           int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out, float* lse,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const tv::AttnShape s = make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream, uint32_t flags = 0) {
+  const tv::AttnShape s = make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype, flags);
   const tv::AttnPlan plan = tv::plan_attention(s);
   if (workspace_bytes < plan.ws_bytes || (plan.ws_bytes > 0 && (workspace == nullptr || !aligned16(workspace))))
     return TV_ERR_INVALID;
@@ -287,16 +291,23 @@ tv_status_t tv_rope_neox(void* x, tv_dtype_t dtype, const int32_t* pos, int64_t 
              : TV_ERR_LAUNCH;
 }
 
-size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_t prefix_len, int32_t d_c,
-                                     int32_t d_r, tv_dtype_t kv_dtype) {
+size_t tv_verify_attn_ex_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_t prefix_len, int32_t d_c,
+                                        int32_t d_r, tv_dtype_t kv_dtype, uint32_t flags) {
+  if (flags & ~kAttnFlags) return 0;
   if (check_attn_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype) != TV_OK) return 0;
-  return tv::plan_attention(make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype)).ws_bytes;
+  return tv::plan_attention(make_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype, flags)).ws_bytes;
 }
 
-tv_status_t tv_verify_attn(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
-                           const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
-                           int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
-                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+size_t tv_verify_attn_workspace_size(int32_t B, int32_t H, int32_t q_len, int32_t prefix_len, int32_t d_c,
+                                     int32_t d_r, tv_dtype_t kv_dtype) {
+  return tv_verify_attn_ex_workspace_size(B, H, q_len, prefix_len, d_c, d_r, kv_dtype, 0);
+}
+
+tv_status_t tv_verify_attn_ex(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                              const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                              int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, uint32_t flags,
+                              float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (flags & ~kAttnFlags) return TV_ERR_INVALID;
   const tv_status_t st = check_attn_shape(prefix_len, B, H, q_len, d_c, d_r, kv_dtype);
   if (st != TV_OK) return st;
   if (!q_lat || !q_rope || !c_kv || !k_rope || !parent || !out) return TV_ERR_INVALID;
@@ -305,7 +316,15 @@ tv_status_t tv_verify_attn(const float* q_lat, const float* q_rope, const void* 
     return TV_ERR_INVALID;
   if (!isfinite(sm_scale)) return TV_ERR_INVALID;
   return run_attention(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, B, H, q_len, d_c, d_r, kv_dtype, sm_scale,
-                       out, lse, workspace, workspace_bytes, stream);
+                       out, lse, workspace, workspace_bytes, stream, flags);
+}
+
+tv_status_t tv_verify_attn(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
+                           const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
+                           int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return tv_verify_attn_ex(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, B, H, q_len, d_c, d_r, kv_dtype,
+                           sm_scale, 0, out, lse, workspace, workspace_bytes, stream);
 }
 
 tv_status_t tv_verify_attn_noalloc(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,

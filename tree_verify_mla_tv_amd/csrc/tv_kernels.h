@@ -35,15 +35,17 @@ hipError_t launch_tree_rope_ragged(float* q_rope, void* k_rope, bool bf16, const
 // ---------------------------------------------------------------------------
 // Attention
 // ---------------------------------------------------------------------------
-enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1, kMfmaF32 = 2 };
+enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1, kMfmaF32 = 2, kMfmaBf16Q2 = 3 };
 
-// Workgroup geometry of the three kernels: the bf16-cache matrix-core kernel
-// (d_c 512, d_r 64), the fp32-cache matrix-core kernel (the same dims) and the
+// Workgroup geometry of the kernels: the bf16-cache matrix-core kernels (d_c
+// 512, d_r 64; queries as two bf16 terms by default, or rounded to one on
+// request), the fp32-cache matrix-core kernel (the same dims) and the
 // vector-ALU kernel (every other supported shape).
 constexpr int kValuRows = 16;     // query rows per workgroup
 constexpr int kValuKeys = 32;     // kv rows per LDS tile
 constexpr int kValuThreads = 256;
-constexpr int kMfmaRows = 128;    // 4 waves x 32 query rows
+constexpr int kMfmaRows = 128;    // 4 waves x 32 query rows (bf16 queries)
+constexpr int kQ2Rows = 64;       // 4 waves x 16 query rows (queries as hi + lo bf16 terms)
 constexpr int kMfmaKeys = 32;
 constexpr int kMfmaThreads = 256;
 constexpr int kF32Rows = 64;      // 4 waves x 16 query rows
@@ -84,6 +86,7 @@ struct AttnPlan {
 struct AttnShape {
   int B, H, q_len, prefix_len, kv_len, d_c, d_r;
   bool kv_bf16;
+  bool bf16_queries;  // bf16 cache at (512, 64): round the scaled queries to one bf16 term
 };
 
 AttnPlan plan_attention(const AttnShape& s);
@@ -418,6 +421,7 @@ hipError_t launch_tree_build(const float* logp, const int32_t* cand_tok, const i
 // Kernel launchers (one per kernel family).
 hipError_t launch_attn_valu(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_mfma_bf16(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_mfma_q2(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_mfma_f32(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
 
 // Ancestor bit masks of one tree: bit m % 64 of word s_anc[i * kAncWords +

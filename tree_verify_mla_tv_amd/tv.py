@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtv.so")
 
 TV_OK, TV_ERR_INVALID, TV_ERR_UNSUPPORTED, TV_ERR_LAUNCH = 0, 1, 2, 3
+TV_ATTN_BF16_QUERIES = 1
 TV_F32, TV_BF16 = 0, 1
 TV_MAX_Q_LEN = 256
 TV_MAX_BUILD_BUDGET = TV_MAX_Q_LEN - 1
@@ -39,6 +40,9 @@ SIGNATURES = {
     "tv_verify_attn": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
                               _sz, _p]),
     "tv_verify_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "tv_verify_attn_ex": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                 ctypes.c_uint32, _p, _p, _p, _sz, _p]),
+    "tv_verify_attn_ex_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_uint32]),
     "tv_verify_attn_noalloc": (_i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p,
                                       _p]),
     "tv_tree_rope": (_i32, [_p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f64, _p]),
@@ -176,7 +180,10 @@ def rope_neox_strided(x: torch.Tensor, pos: torch.Tensor | None = None, theta: f
     return x
 
 
-def workspace_size(B: int, H: int, q_len: int, prefix_len: int, d_c: int, d_r: int, kv_dtype: int) -> int:
+def workspace_size(B: int, H: int, q_len: int, prefix_len: int, d_c: int, d_r: int, kv_dtype: int,
+                   flags: int = 0) -> int:
+    if flags:
+        return int(load().tv_verify_attn_ex_workspace_size(B, H, q_len, prefix_len, d_c, d_r, kv_dtype, flags))
     return int(load().tv_verify_attn_workspace_size(B, H, q_len, prefix_len, d_c, d_r, kv_dtype))
 
 
@@ -217,21 +224,34 @@ def _outputs(q_lat, out, lse, return_lse, workspace, ws_bytes):
 
 def verify_attn(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, sm_scale: float | None = None, out=None,
                 lse=None, return_lse: bool = False, workspace=None):
-    """Tree-verify MLA-absorb attention (rope slices already rotated).
+    """Tree-verify MLA-absorb attention (rope slices already rotated): tv_verify_attn.
 
     Returns out [B, q_len, H, d_c] float32 (and lse [B, q_len, H] if asked or given).
     sm_scale defaults to 1/sqrt(d_c + d_r), rounded to fp32.
     """
+    return verify_attn_ex(q_lat, q_rope, c_kv, k_rope, parent, prefix_len, sm_scale, 0, out, lse, return_lse,
+                          workspace)
+
+
+def verify_attn_ex(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, sm_scale: float | None = None,
+                   flags: int = 0, out=None, lse=None, return_lse: bool = False, workspace=None):
+    """verify_attn with option flags (tv_verify_attn_ex; flags 0 calls
+    tv_verify_attn).  TV_ATTN_BF16_QUERIES rounds the scaled queries to one
+    bf16 term on the bf16-cache matrix-core path."""
     B, q, H, d_c, d_r = _attn_shapes(q_lat, q_rope, c_kv, k_rope, parent, prefix_len)
     dt = _kv_dtype(c_kv)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d_c + d_r)
-    ws_bytes = workspace_size(B, H, q, prefix_len, d_c, d_r, dt)
+    ws_bytes = workspace_size(B, H, q, prefix_len, d_c, d_r, dt, flags)
     out, lse_t, workspace = _outputs(q_lat, out, lse, return_lse, workspace, ws_bytes)
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("tv_verify_attn", load().tv_verify_attn(
-        _ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
-        float(sm_scale), _ptr(out), _ptr(lse_t), _ptr(workspace), ws_n, _stream()))
+    head = (_ptr(q_lat), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), _ptr(parent), prefix_len, B, H, q, d_c, d_r, dt,
+            float(sm_scale))
+    tail = (_ptr(out), _ptr(lse_t), _ptr(workspace), ws_n, _stream())
+    if flags:
+        _check("tv_verify_attn_ex", load().tv_verify_attn_ex(*head, flags, *tail))
+    else:
+        _check("tv_verify_attn", load().tv_verify_attn(*head, *tail))
     return (out, lse_t) if (return_lse or lse is not None) else out
 
 
