@@ -468,3 +468,32 @@ def test_bf16_queries_serving_scale():
                                  tv.TV_ATTN_BF16_QUERIES, return_lse=True)
     torch.cuda.synchronize()
     check_out(w.name + " bf16 queries", w.describe(), out, lse, ref["out"], ref["lse"], "bf16")
+
+
+@pytest.mark.parametrize("d_r,H,dt", [(6, 3, "f32"), (32, 8, "bf16"), (64, 64, "bf16"), (128, 1, "f32"),
+                                      (64, 600, "f32"), (2, 5, "bf16")])
+def test_tree_rope_shapes(d_r, H, dt):
+    """tv_tree_rope on its own over row widths and head counts that take each
+    path of the kernel (whole 16-byte items, one pair at a time, more items
+    than a workgroup prefetches, several nodes per workgroup): query rows and
+    the tree's key rows turn at prefix + depth like the oracle's rotation;
+    the prefix key rows are untouched."""
+    rng = np.random.default_rng(d_r * 1000 + H)
+    B, q, P = 3, 33, 50
+    qr = rng.standard_normal((B, q, H, d_r), dtype=np.float32)
+    kr = rng.standard_normal((B, P + q, d_r), dtype=np.float32)
+    if dt == "bf16":
+        kr = W.f32_to_bf16_bits(kr)
+    parent = np.stack([W.tree_rrt(q, rng) for _ in range(B)]).astype(np.int32)
+    qt, kt = cuda_f32(qr), cuda_cache(kr, dt)
+    tv.tree_rope(qt, kt, torch.from_numpy(parent).cuda(), P, 10000.0)
+    torch.cuda.synchronize()
+    pos_q = O.node_positions(parent, P)
+    ref_q = O.rope_neox_stored(O.as_f64(qr, "f32"), pos_q[:, :, None], 10000.0, "f32")
+    ref_k = O.rope_neox_stored(O.as_f64(kr, dt)[:, P:], pos_q, 10000.0, dt)
+    got_k = O.as_f64(cache_numpy(kt, dt), dt)
+    mp = int(pos_q.max())
+    nq = rope_mismatch(qt.cpu().numpy(), ref_q, O.as_f64(qr, "f32"), "f32", mp)
+    nk = rope_mismatch(got_k[:, P:], ref_k, O.as_f64(kr, dt)[:, P:], dt, mp)
+    assert nq[0] == 0 and nq[1] <= 1e-3 and nk[0] == 0 and nk[1] <= 1e-3, (nq, nk)
+    assert np.array_equal(got_k[:, :P], O.as_f64(kr, dt)[:, :P])

@@ -78,27 +78,40 @@ __global__ __launch_bounds__(64) void tree_positions_kernel(const int32_t* __res
   for (int i = threadIdx.x; i < q_len; i += blockDim.x) pos[static_cast<int64_t>(b) * q_len + i] = prefix_len + s_depth[i];
 }
 
-// The step's rotation: for tree b (blockIdx.y) and node i (blockIdx.x), the
-// node's H query rows q_rope[b,i,h,:] and the tree's own key row
-// k_rope[b, prefix+i, :] turn at prefix + depth(i).  Every row of a node shares
-// its angles, so the block evaluates the float64 cos/sin of each pair once (in
-// LDS) and rotates the H + 1 rows with them: the same values, rounded the same
-// way, as evaluating them per row.  A ragged batch (req non-null) takes each
-// request's node range, node count and prefix from its record; its query rows
-// are packed request after request and its key rows start at b * kv_len
-// (kv_len = the cache stride).
-template <typename KV>
-__global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_rope,
-                                                        typename KV::storage* __restrict__ k_rope,
-                                                        const int32_t* __restrict__ parent, int q_len, int H,
-                                                        int half, int prefix_len, int kv_len, RopeFreq f,
-                                                        const int32_t* __restrict__ req) {
+// The step's rotation: for tree b (blockIdx.y) and the nodes i0 .. i0 + npb - 1
+// of group blockIdx.x (i0 = npb * blockIdx.x), each node's H query rows
+// q_rope[b,i,h,:] and the tree's own key row k_rope[b, prefix+i, :] turn at
+// prefix + depth(i).  Every row of a node shares its angles, so the block
+// evaluates each node's float64 cos/sin once (in LDS) and rotates its H + 1
+// rows with them: the same values, rounded the same way, as evaluating them
+// per row.  The query rows are the traffic (H rows per node against one key
+// row): each thread first issues the loads of up to kRopePrefetch items (an
+// item = 4 consecutive pairs of one row, 16 bytes of each half) into
+// registers, then the block walks the parent chains and evaluates the angles
+// while those loads are in flight, then rotates and stores.  Items past the
+// prefetch (only when npb * H * half / 4 exceeds 256 kRopePrefetch) and rows
+// whose half is not a multiple of 4 take a plain loop.  A ragged batch (req
+// non-null) takes each request's node range, node count and prefix from its
+// record; its query rows are packed request after request and its key rows
+// start at b * kv_len (kv_len = the cache stride).
+constexpr int kRopeThreads = 256;
+constexpr int kRopePrefetch = 2;
+constexpr int kRopeMaxNodes = 8;
+static_assert(kMaxQ <= kRopeThreads && kRopeMaxNodes * kMaxHalf <= 2 * kRopeThreads,
+              "one parent and at most two angles per thread");
+
+template <typename KV, bool VEC>
+__global__ __launch_bounds__(kRopeThreads) void tree_rope_kernel(float* __restrict__ q_rope,
+                                                                 typename KV::storage* __restrict__ k_rope,
+                                                                 const int32_t* __restrict__ parent, int q_len,
+                                                                 int H, int half, int prefix_len, int kv_len,
+                                                                 int npb, RopeFreq f,
+                                                                 const int32_t* __restrict__ req) {
   __shared__ int s_parent[kMaxQ];
-  __shared__ double s_cos[kMaxHalf];
-  __shared__ double s_sin[kMaxHalf];
-  __shared__ int s_depth;
+  __shared__ int s_depth[kRopeMaxNodes];
+  __shared__ double s_cs[kRopeMaxNodes][kMaxHalf][2];
   const int b = blockIdx.y;
-  const int i = blockIdx.x;
+  const int i0 = blockIdx.x * npb;
   int64_t node0 = static_cast<int64_t>(b) * q_len;
   if (req) {
     const int32_t* r = req + b * kReqFields;
@@ -106,43 +119,138 @@ __global__ __launch_bounds__(256) void tree_rope_kernel(float* __restrict__ q_ro
     q_len = r[kReqQLen];
     prefix_len = r[kReqPrefix];
   }
-  if (i >= q_len) return;  // the whole block
-  // Node i's ancestors all have indices below i (parents are clamped).
-  for (int j = threadIdx.x; j <= i; j += blockDim.x) s_parent[j] = clamp_parent(parent[node0 + j], j);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int d = 0;
-    for (int n = s_parent[i]; n >= 0; n = s_parent[n]) ++d;
-    s_depth = d;
-  }
-  __syncthreads();
-  const double pos = static_cast<double>(prefix_len + s_depth);
-  for (int k = threadIdx.x; k < half; k += blockDim.x) {
-    double sn, cs;
-    sincos(pos * f.inv_freq[k], &sn, &cs);
-    s_sin[k] = sn;
-    s_cos[k] = cs;
-  }
-  __syncthreads();
-  const int per_node = (H + 1) * half;
-  for (int idx = threadIdx.x; idx < per_node; idx += blockDim.x) {
-    const int h = idx / half;
-    const int k = idx - h * half;
-    const double c = s_cos[k];
-    const double sn = s_sin[k];
-    double y1, y2;
-    if (h < H) {
-      float* row = q_rope + ((node0 + i) * H + h) * 2 * half;
-      rotate_cs_f64(static_cast<double>(row[k]), static_cast<double>(row[k + half]), c, sn, y1, y2);
-      row[k] = static_cast<float>(y1);
-      row[k + half] = static_cast<float>(y2);
-    } else {
-      typename KV::storage* row = k_rope + (static_cast<int64_t>(b) * kv_len + prefix_len + i) * 2 * half;
-      rotate_cs_f64(load_f64<KV>(row + k), load_f64<KV>(row + k + half), c, sn, y1, y2);
-      store_from_f64<KV>(row + k, y1);
-      store_from_f64<KV>(row + k + half, y2);
+  if (i0 >= q_len) return;  // the whole block
+  const int nn = min(npb, q_len - i0);
+  const int t = threadIdx.x;
+  const int i_end = i0 + nn;   // <= q_len <= kMaxQ = 256 = kRopeThreads: one parent per thread
+  const int n_ang = nn * half;  // angles of the block: at most 2 per thread
+
+  // What the angle phase reads is loaded first: memory waits count loads in
+  // issue order, so waiting for these does not wait for the row loads below.
+  const int par = parent[node0 + min(t, i_end - 1)];
+  const double fr0 = f.inv_freq[min(t, n_ang - 1) % half];
+  const double fr1 = f.inv_freq[min(t + kRopeThreads, n_ang - 1) % half];
+
+  // Query rows of the block's nodes: contiguous, nn * H rows of 2 * half floats.
+  float* const q0 = q_rope + (node0 + i0) * H * 2 * half;
+  // VEC: half is a multiple of 4 (the host's choice), items of 16 bytes.
+  const int qpr = half >> 2;                          // items per row
+  const int items = VEC ? nn * H * qpr : 0;
+  // The loads are unconditional (items past the end re-read the last item, and
+  // only in-range items are stored), so they all issue before any wait.
+  float4 x1[kRopePrefetch], x2[kRopePrefetch];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < kRopePrefetch; ++k) {
+      const int it = min(t + k * kRopeThreads, items - 1);
+      const int row = it / qpr, c = it - row * qpr;
+      const float* rp = q0 + static_cast<int64_t>(row) * 2 * half + 4 * c;
+      x1[k] = *reinterpret_cast<const float4*>(rp);
+      x2[k] = *reinterpret_cast<const float4*>(rp + half);
     }
   }
+
+
+  // Depths (ancestors have lower indices: parents are clamped) and angles.
+  s_parent[t] = t < i_end ? clamp_parent(par, t) : -1;  // unconditional: the load stays where it is
+  __syncthreads();
+  if (t < nn) {
+    int d = 0;
+    for (int n = s_parent[i0 + t]; n >= 0; n = s_parent[n]) ++d;
+    s_depth[t] = d;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int j = t + r * kRopeThreads;
+    if (j < n_ang) {
+      const int n = j / half, k = j - n * half;
+      double sn, cs;
+      sincos(static_cast<double>(prefix_len + s_depth[n]) * (r == 0 ? fr0 : fr1), &sn, &cs);
+      s_cs[n][k][0] = cs;
+      s_cs[n][k][1] = sn;
+    }
+  }
+  __syncthreads();
+  // The loaded values are first used here.  The empty asm hands them over
+  // as if redefined at this point, so the compiler cannot move their float64
+  // conversions up next to the loads (where the waits for the data would
+  // serialise the loads behind each other).
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < kRopePrefetch; ++k) {
+      asm volatile("" : "+v"(x1[k].x), "+v"(x1[k].y), "+v"(x1[k].z), "+v"(x1[k].w));
+      asm volatile("" : "+v"(x2[k].x), "+v"(x2[k].y), "+v"(x2[k].z), "+v"(x2[k].w));
+    }
+  }
+
+  auto rot = [&](float a1, float a2, int n, int k, float& y1, float& y2) {
+    double r1, r2;
+    rotate_cs_f64(static_cast<double>(a1), static_cast<double>(a2), s_cs[n][k][0], s_cs[n][k][1], r1, r2);
+    y1 = static_cast<float>(r1);
+    y2 = static_cast<float>(r2);
+  };
+#pragma unroll
+  for (int k = 0; k < kRopePrefetch; ++k) {
+    const int it = t + k * kRopeThreads;
+    if (it < items) {
+      const int row = it / qpr, c = it - row * qpr;
+      const int n = row / H, kk = 4 * c;
+      float4 y1, y2;
+      rot(x1[k].x, x2[k].x, n, kk + 0, y1.x, y2.x);
+      rot(x1[k].y, x2[k].y, n, kk + 1, y1.y, y2.y);
+      rot(x1[k].z, x2[k].z, n, kk + 2, y1.z, y2.z);
+      rot(x1[k].w, x2[k].w, n, kk + 3, y1.w, y2.w);
+      float* rp = q0 + static_cast<int64_t>(row) * 2 * half + kk;
+      *reinterpret_cast<float4*>(rp) = y1;
+      *reinterpret_cast<float4*>(rp + half) = y2;
+    }
+  }
+  // The rest of the query rows: items past the prefetch, or one pair at a
+  // time when half is not a multiple of 4.
+  if constexpr (VEC) {
+    for (int it = t + kRopePrefetch * kRopeThreads; it < items; it += kRopeThreads) {
+      const int row = it / qpr, c = it - row * qpr;
+      const int n = row / H, kk = 4 * c;
+      float* rp = q0 + static_cast<int64_t>(row) * 2 * half + kk;
+      const float4 a1 = *reinterpret_cast<const float4*>(rp);
+      const float4 a2 = *reinterpret_cast<const float4*>(rp + half);
+      float4 y1, y2;
+      rot(a1.x, a2.x, n, kk + 0, y1.x, y2.x);
+      rot(a1.y, a2.y, n, kk + 1, y1.y, y2.y);
+      rot(a1.z, a2.z, n, kk + 2, y1.z, y2.z);
+      rot(a1.w, a2.w, n, kk + 3, y1.w, y2.w);
+      *reinterpret_cast<float4*>(rp) = y1;
+      *reinterpret_cast<float4*>(rp + half) = y2;
+    }
+  } else {
+    for (int it = t; it < nn * H * half; it += kRopeThreads) {
+      const int row = it / half, k = it - row * half;
+      float* rp = q0 + static_cast<int64_t>(row) * 2 * half;
+      float y1, y2;
+      rot(rp[k], rp[k + half], row / H, k, y1, y2);
+      rp[k] = y1;
+      rp[k + half] = y2;
+    }
+  }
+  // The tree's own key rows.
+  for (int j = t; j < nn * half; j += kRopeThreads) {
+    const int n = j / half, k = j - n * half;
+    typename KV::storage* row = k_rope + (static_cast<int64_t>(b) * kv_len + prefix_len + i0 + n) * 2 * half;
+    double y1, y2;
+    rotate_cs_f64(load_f64<KV>(row + k), load_f64<KV>(row + k + half), s_cs[n][k][0], s_cs[n][k][1], y1, y2);
+    store_from_f64<KV>(row + k, y1);
+    store_from_f64<KV>(row + k + half, y2);
+  }
+}
+
+// Nodes per workgroup: as many as keep the block's query items within the
+// prefetch (at most kRopeMaxNodes, at least one).
+inline int rope_nodes_per_block(int H, int half) {
+  const int qpr = (half & 3) == 0 ? half / 4 : half;
+  const long long per_node = static_cast<long long>(H) * qpr;
+  long long n = static_cast<long long>(kRopeThreads) * kRopePrefetch / (per_node > 0 ? per_node : 1);
+  return static_cast<int>(n < 1 ? 1 : (n > kRopeMaxNodes ? kRopeMaxNodes : n));
 }
 
 // ---------------------------------------------------------------------------
@@ -173,17 +281,30 @@ hipError_t launch_tree_positions(const int32_t* parent, int B, int q_len, int pr
   return hipGetLastError();
 }
 
+template <typename KV>
+void tree_rope_launch(const dim3& grid, float* q_rope, typename KV::storage* k_rope, const int32_t* parent, int q_len,
+                      int H, int half, int prefix_len, int kv_len, int npb, const RopeFreq& f, const int32_t* req,
+                      hipStream_t stream) {
+  if ((half & 3) == 0)
+    tree_rope_kernel<KV, true><<<grid, kRopeThreads, 0, stream>>>(q_rope, k_rope, parent, q_len, H, half, prefix_len,
+                                                                  kv_len, npb, f, req);
+  else
+    tree_rope_kernel<KV, false><<<grid, kRopeThreads, 0, stream>>>(q_rope, k_rope, parent, q_len, H, half, prefix_len,
+                                                                   kv_len, npb, f, req);
+}
+
 hipError_t launch_tree_rope(float* q_rope, void* k_rope, bool bf16, const int32_t* parent, int B, int q_len, int H,
                             int d_r, int prefix_len, const RopeFreq& f, hipStream_t stream) {
   const int half = d_r / 2;
   const int kv_len = prefix_len + q_len;
-  const dim3 grid(static_cast<unsigned>(q_len), static_cast<unsigned>(B));
+  const int npb = rope_nodes_per_block(H, half);
+  const dim3 grid(static_cast<unsigned>((q_len + npb - 1) / npb), static_cast<unsigned>(B));
   if (bf16)
-    tree_rope_kernel<BF16><<<grid, 256, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, q_len, H, half,
-                                                     prefix_len, kv_len, f, nullptr);
+    tree_rope_launch<BF16>(grid, q_rope, static_cast<uint16_t*>(k_rope), parent, q_len, H, half, prefix_len, kv_len,
+                           npb, f, nullptr, stream);
   else
-    tree_rope_kernel<F32><<<grid, 256, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, q_len, H, half,
-                                                    prefix_len, kv_len, f, nullptr);
+    tree_rope_launch<F32>(grid, q_rope, static_cast<float*>(k_rope), parent, q_len, H, half, prefix_len, kv_len, npb,
+                          f, nullptr, stream);
   return hipGetLastError();
 }
 
@@ -191,13 +312,14 @@ hipError_t launch_tree_rope_ragged(float* q_rope, void* k_rope, bool bf16, const
                                    int B, int max_q, int H, int d_r, int kv_stride, const RopeFreq& f,
                                    hipStream_t stream) {
   const int half = d_r / 2;
-  const dim3 grid(static_cast<unsigned>(max_q), static_cast<unsigned>(B));
+  const int npb = rope_nodes_per_block(H, half);
+  const dim3 grid(static_cast<unsigned>((max_q + npb - 1) / npb), static_cast<unsigned>(B));
   if (bf16)
-    tree_rope_kernel<BF16><<<grid, 256, 0, stream>>>(q_rope, static_cast<uint16_t*>(k_rope), parent, max_q, H, half,
-                                                     0, kv_stride, f, req);
+    tree_rope_launch<BF16>(grid, q_rope, static_cast<uint16_t*>(k_rope), parent, max_q, H, half, 0, kv_stride, npb,
+                           f, req, stream);
   else
-    tree_rope_kernel<F32><<<grid, 256, 0, stream>>>(q_rope, static_cast<float*>(k_rope), parent, max_q, H, half, 0,
-                                                    kv_stride, f, req);
+    tree_rope_launch<F32>(grid, q_rope, static_cast<float*>(k_rope), parent, max_q, H, half, 0, kv_stride, npb, f,
+                          req, stream);
   return hipGetLastError();
 }
 
