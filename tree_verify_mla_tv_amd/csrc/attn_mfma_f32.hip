@@ -66,8 +66,10 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
 // This thread's share of half h of key tile [kt, kt + 32): row 16 h + t / 16
 // of the tile, float4 columns t % 16 + 16 i (i < 8: the latent row, 256 bytes
 // apart) and the rope row's float4 t % 16, so a thread keeps two base
-// addresses.  Rows past the unit's range end read the last row and store 0.
-__device__ __forceinline__ void load_half(const AttnArgs& a, const Unit& w, int kt, int h,
+// addresses.  Rows past the unit's range end read the last row; they are
+// stored as 0 (store_half), the select made at the store so that the loads
+// do not wait.  Returns whether the row is in range.
+__device__ __forceinline__ bool load_half(const AttnArgs& a, const Unit& w, int kt, int h,
                                           float4 (&r)[kHalfChunks]) {
   const int row = 16 * h + (threadIdx.x >> 4);
   const int cg = threadIdx.x & 15;
@@ -75,23 +77,22 @@ __device__ __forceinline__ void load_half(const AttnArgs& a, const Unit& w, int 
   const int64_t krow = w.kv_row0 + min(key, w.k_end - 1);
   const float* lat = static_cast<const float*>(a.c_kv) + krow * DC + 4 * cg;
   const float* rope = static_cast<const float*>(a.k_rope) + krow * DR + 4 * cg;
-  const bool in = key < w.k_end;
-  // (component-wise selects: a select of whole float4s was compiled through
-  // private memory)
 #pragma unroll
-  for (int i = 0; i < DC / 64; ++i) {
-    const float4 v = *reinterpret_cast<const float4*>(lat + 64 * i);
-    r[i] = make_float4(in ? v.x : 0.f, in ? v.y : 0.f, in ? v.z : 0.f, in ? v.w : 0.f);
-  }
-  const float4 v = *reinterpret_cast<const float4*>(rope);
-  r[DC / 64] = make_float4(in ? v.x : 0.f, in ? v.y : 0.f, in ? v.z : 0.f, in ? v.w : 0.f);
+  for (int i = 0; i < DC / 64; ++i) r[i] = *reinterpret_cast<const float4*>(lat + 64 * i);
+  r[DC / 64] = *reinterpret_cast<const float4*>(rope);
+  return key < w.k_end;
 }
 
-__device__ __forceinline__ void store_half(float* buf, int h, const float4 (&r)[kHalfChunks]) {
+// (component-wise selects: a select of whole float4s was compiled through
+// private memory)
+__device__ __forceinline__ void store_half(float* buf, int h, const float4 (&r)[kHalfChunks], bool in) {
   float* dst = buf + (16 * h + (threadIdx.x >> 4)) * kStride + 4 * (threadIdx.x & 15);
 #pragma unroll
-  for (int i = 0; i < DC / 64; ++i) *reinterpret_cast<float4*>(dst + 64 * i) = r[i];
-  *reinterpret_cast<float4*>(dst + DC) = r[DC / 64];
+  for (int i = 0; i <= DC / 64; ++i) {
+    const float4 v = r[i];
+    *reinterpret_cast<float4*>(dst + (i < DC / 64 ? 64 * i : DC)) =
+        make_float4(in ? v.x : 0.f, in ? v.y : 0.f, in ? v.z : 0.f, in ? v.w : 0.f);
+  }
 }
 
 }  // namespace
@@ -119,40 +120,74 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
   const bool row_valid = row < w.R;
   const int node = min(row / a.H, w.q_len - 1);
 
+  const int n_tiles = (w.k_end - w.k_begin + kF32Keys - 1) / kF32Keys;
+  // The block's 64 query rows come in coalesced (consecutive threads read
+  // consecutive 16-byte pieces of a row; rows past R read row 0 of the tree)
+  // and go to the idle tile buffers at the tile's row pitch; each lane then
+  // reads its quarter back.  (Read straight from HBM, each lane's quarter made
+  // every load instruction touch 64 separate pieces of 16 rows.)  The first
+  // key tile's first half is requested with them, and the tree's ancestor
+  // masks are built while both are in flight.
+  static_assert(kF32Rows * kStride <= 2 * kTileFloats, "the query block fits the tile buffers");
+  static_assert(kMaxQ <= kF32Threads, "one parent per thread");
+  constexpr int kQChunks = kF32Rows * (D / 4) / kF32Threads;  // 36 float4 per thread
+  // Every load of the prologue is issued before the first wait, queries
+  // first (waits count loads in issue order): one memory round trip instead
+  // of one per batch.
+  floatx4 x[kQChunks];
+#pragma unroll
+  for (int i = 0; i < kQChunks; ++i) {
+    const int idx = threadIdx.x + kF32Threads * i;
+    const int r = idx / (D / 4), d = 4 * (idx - r * (D / 4));
+    const int gr = w.rb * kF32Rows + r;
+    const int64_t grow = w.row0 + (gr < w.R ? gr : 0);
+    const float* src = d < DC ? a.q_lat + grow * DC + d : a.q_rope + grow * DR + (d - DC);
+    x[i] = *reinterpret_cast<const floatx4*>(src);
+  }
+  float4 pre[kHalfChunks];
+  bool pre_in = false;
+  if (n_tiles > 0) pre_in = load_half(a, w, w.k_begin, 0, pre);
+  const int par_t = a.parent[w.par0 + min(static_cast<int>(threadIdx.x), w.q_len - 1)];
+  // Every load above is issued before anything waits: the empty asm (with a
+  // memory clobber) keeps the loads above it and the LDS stores below it, and
+  // hands over the query values there.  (Left alone, the compiler paired each
+  // load with its store and waited for each in turn.)
+#pragma unroll
+  for (int i = 0; i < kQChunks; i += 4) asm volatile("" : "+v"(x[i]), "+v"(x[i + 1]), "+v"(x[i + 2]), "+v"(x[i + 3])::"memory");
+#pragma unroll
+  for (int i = 0; i < kQChunks; ++i) {
+    const int idx = threadIdx.x + kF32Threads * i;
+    const int r = idx / (D / 4), d = 4 * (idx - r * (D / 4));
+    *reinterpret_cast<floatx4*>(sK + r * kStride + d) = x[i];
+  }
+  build_ancestors_loaded(par_t, w.q_len, s_par, s_anc);  // ends with a barrier: the query block is in LDS
   // Query quarter lg of this lane's row: d = 144 lg + s, scaled; zero past R.
   float qf[kQuarter];
   {
     const float sc = row_valid ? a.sm_scale * kLog2e : 0.f;
-    const int64_t grow = w.row0 + (row_valid ? row : 0);
+    const float* qs = sK + r_blk * kStride + lg * kQuarter;
 #pragma unroll
     for (int c = 0; c < kQuarter / 4; ++c) {
-      const int d = lg * kQuarter + 4 * c;
-      const float* src = d < DC ? a.q_lat + grow * DC + d : a.q_rope + grow * DR + (d - DC);
-      const float4 x = *reinterpret_cast<const float4*>(src);
+      const float4 x = *reinterpret_cast<const float4*>(qs + 4 * c);
       qf[4 * c] = x.x * sc;
       qf[4 * c + 1] = x.y * sc;
       qf[4 * c + 2] = x.z * sc;
       qf[4 * c + 3] = x.w * sc;
     }
   }
+  __syncthreads();  // the tile buffers are free again
 
-  const int n_tiles = (w.k_end - w.k_begin + kF32Keys - 1) / kF32Keys;
   float m_ref = -INFINITY, m_seen = -INFINITY, exc = -INFINITY, l_run = 0.f;
   floatx4 o[DC / 16];
-  // The first key tile's first half is requested with the query loads, and the
-  // tree's ancestor masks are built while both are in flight.
-  float4 pre[kHalfChunks];
-  if (n_tiles > 0) load_half(a, w, w.k_begin, 0, pre);
-  build_ancestors(a.parent + w.par0, w.q_len, s_par, s_anc);
   for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int j = 0; j < DC / 16; ++j) o[j] = floatx4{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
     if (n_tiles > 0) {
-      if (pass > 0) load_half(a, w, w.k_begin, 0, pre);
-      store_half(sK, 0, pre);
-      load_half(a, w, w.k_begin, 1, pre);
-      store_half(sK, 1, pre);
+      if (pass > 0) pre_in = load_half(a, w, w.k_begin, 0, pre);
+      store_half(sK, 0, pre, pre_in);
+      pre_in = load_half(a, w, w.k_begin, 1, pre);
+      store_half(sK, 1, pre, pre_in);
     }
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
@@ -163,7 +198,7 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
       const float* cur = sK + (t & 1) * kTileFloats;
       float* nxt = sK + ((t + 1) & 1) * kTileFloats;
       const bool more = t + 1 < n_tiles;
-      if (more) load_half(a, w, kt + kF32Keys, 0, pre);
+      if (more) pre_in = load_half(a, w, kt + kF32Keys, 0, pre);
 
       // Scores: block b holds keys 16 b + 4 lg + v (register v) of row ln.
       floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -185,8 +220,8 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
         }
       }
       if (more) {
-        store_half(nxt, 0, pre);
-        load_half(a, w, kt + kF32Keys, 1, pre);
+        store_half(nxt, 0, pre, pre_in);
+        pre_in = load_half(a, w, kt + kF32Keys, 1, pre);
       }
       float p[8];
 #pragma unroll
@@ -223,7 +258,7 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
 
       // The next tile's second half goes to LDS before the value product, so
       // its registers are free for the value operands.
-      if (more) store_half(nxt, 1, pre);
+      if (more) store_half(nxt, 1, pre, pre_in);
 
       // Values: contraction step (b, v) takes key 16 b + 4 lg + v of lane group
       // lg.  Output block 4 m + r holds d = 64 m + 4 x + r in its row x, so a

@@ -445,6 +445,26 @@ __device__ __forceinline__ void build_ancestors(const int32_t* __restrict__ pare
   __syncthreads();
 }
 
+// build_ancestors for a workgroup of at least q_len threads whose thread t
+// already holds parent[t] (any value for t >= q_len): the parent loads can be
+// issued early, ahead of other loads, and waited for here.  Ends with a barrier.
+__device__ __forceinline__ void build_ancestors_loaded(int par_t, int q_len, int* s_par,
+                                                       unsigned long long* s_anc) {
+  if (static_cast<int>(threadIdx.x) < q_len) s_par[threadIdx.x] = clamp_parent(par_t, threadIdx.x);
+  __syncthreads();
+  for (int i = threadIdx.x; i < q_len; i += blockDim.x) {
+    unsigned long long w[kAncWords] = {};
+    for (int n = i; n >= 0; n = s_par[n]) {
+      const unsigned long long bit = 1ull << (n & 63);
+#pragma unroll
+      for (int k = 0; k < kAncWords; ++k) w[k] |= (n >> 6) == k ? bit : 0ull;
+    }
+#pragma unroll
+    for (int k = 0; k < kAncWords; ++k) s_anc[i * kAncWords + k] = w[k];
+  }
+  __syncthreads();
+}
+
 // Whether tree key rel (0 <= rel < q_len) is visible from node `node`.
 __device__ __forceinline__ bool anc_bit(const unsigned long long* s_anc, int node, int rel) {
   return ((s_anc[node * kAncWords + (rel >> 6)] >> (rel & 63)) & 1ull) != 0ull;
