@@ -150,6 +150,38 @@ def _time_ms(torch, fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+SMALL_ROWS = [(1, 1, 1, 5000), (1, 1, 1, 32768), (4, 1, 1, 8192), (1, 16, 1, 8192), (1, 16, 2, 8192),
+              (1, 64, 1, 8192), (8, 8, 1, 4096), (32, 1, 1, 8192), (32, 16, 1, 8192)]
+
+
+def small_rows(torch, tv, W) -> dict:
+    """bf16-cache attention (d_c 512, d_r 64) at small R = H x q_len, the
+    library's own kernel choice: us per call (HIP events around 50 calls) and
+    the cache stream rate."""
+    import numpy as np
+    out = {}
+    for B, H, q, P in SMALL_ROWS:
+        rng = np.random.default_rng(0)
+        kv = P + q
+        gen = torch.Generator(device="cuda").manual_seed(0)
+        ql = torch.randn(B, q, H, 512, device="cuda", generator=gen) * 0.5
+        qr = torch.randn(B, q, H, 64, device="cuda", generator=gen) * 0.5
+        ck = (torch.randn(B, kv, 512, device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+        kr = (torch.randn(B, kv, 64, device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+        par = torch.from_numpy(np.stack([W.tree_branch(q, rng) for _ in range(B)]).astype(np.int32)).cuda()
+        o = torch.empty_like(ql)
+        ws = torch.empty(max(tv.workspace_size(B, H, q, P, 512, 64, tv.TV_BF16), 1), dtype=torch.uint8,
+                         device="cuda")
+        f = lambda: tv.verify_attn(ql, qr, ck, kr, par, P, 0.04, out=o, workspace=ws)
+        for _ in range(20):
+            f()
+        us = _time_ms(torch, f, 50) * 1e3
+        cache_bytes = B * kv * 576 * 2
+        out[f"b{B}_h{H}_q{q}_p{P}"] = {"R": H * q, "us": round(us, 2),
+                                      "cache_tbs": round(cache_bytes / (us * 1e-6) / 1e12, 3)}
+    return out
+
+
 def rope_back_to_back(torch, fn, n: int) -> float:
     """Mean ms per launch of n launches of fn captured in one graph."""
     fn()
@@ -362,6 +394,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the reference launch that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
+    ap.add_argument("--small-rows", action="store_true",
+                    help="only time the bf16-cache attention at small H x q_len (decode-like shapes, where the "
+                         "products are far from dense), print one JSON line and exit")
     ap.add_argument("--fp32-configs", action="store_true",
                     help="only time the fp32-cache configurations (next_rows.fp32_configs), print them as one "
                          "JSON line and exit")
@@ -385,6 +420,9 @@ def main() -> int:
 
     if args.fp32_configs:
         print(json.dumps({"fp32_configs": fp32_configs(torch, tv, W)}), flush=True)
+        return 0
+    if args.small_rows:
+        print(json.dumps({"small_rows": small_rows(torch, tv, W)}), flush=True)
         return 0
 
     w = W.WORKLOADS[args.workload or W.SERVING]
