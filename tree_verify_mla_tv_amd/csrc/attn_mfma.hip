@@ -103,7 +103,7 @@ __device__ __forceinline__ void step(const StepBufs& sb, const TreeKv& kv, const
                : TV_STEP_CLOBBERS, "vcc", "scc", "memory");
 }
 
-__global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_mfma_bf16_unit(const AttnArgs& a, const Unit& w) {
   __shared__ int s_par[kMaxQ];
   __shared__ unsigned long long s_anc[kMaxQ * kAncWords];
   __shared__ __align__(16) unsigned char s_qrope[kMfmaRows * mf::DR * 2];  // 16 KB
@@ -114,12 +114,6 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g2 = lane >> 5;
-  Unit w;
-  if (a.req) {
-    if (!decode_unit_ragged(a, blockIdx.x, w)) return;  // past the batch's units (whole workgroup)
-  } else {
-    w = decode_unit(a, unit_of_block(a, blockIdx.x));
-  }
   const int P = w.P;
   // Raw buffers over this tree's rows (the host keeps kv_len * 1024 below
   // 2^31, so every offset fits in 32 bits).
@@ -316,8 +310,22 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   }
 }
 
+// A uniform batch: one unit per workgroup.
+__global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArgs a) {
+  attn_mfma_bf16_unit(a, decode_unit(a, unit_of_block(a, blockIdx.x)));
+}
+
+// A ragged batch: a persistent grid taking units from its XCD's counter.
+__global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_ragged_kernel(AttnArgs) {
+  for_each_ragged_unit([](const AttnArgs& a, const Unit& w) { attn_mfma_bf16_unit(a, w); });
+}
+
 hipError_t launch_attn_mfma_bf16(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  attn_mfma_bf16_kernel<<<dim3(static_cast<unsigned>(plan.units)), kMfmaThreads, 0, stream>>>(a);
+  const dim3 grid(static_cast<unsigned>(plan.units));
+  if (a.req)
+    attn_mfma_bf16_ragged_kernel<<<grid, kMfmaThreads, 0, stream>>>(a);
+  else
+    attn_mfma_bf16_kernel<<<grid, kMfmaThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -97,7 +97,7 @@ __device__ __forceinline__ void store_half(float* buf, int h, const float4 (&r)[
 
 }  // namespace
 
-__global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_mfma_f32_unit(const AttnArgs& a, const Unit& w) {
   __shared__ __align__(16) float sK[2 * kTileFloats];  // two key tiles: the one in use and the next
   __shared__ int s_par[kMaxQ];
   __shared__ unsigned long long s_anc[kMaxQ * kAncWords];
@@ -107,12 +107,6 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
   const int wave = threadIdx.x >> 6;
   const int ln = lane & 15;  // query row within the wave's 16; key / d within a 16-block
   const int lg = lane >> 4;  // lane group: contraction quarter (scores), key group (values)
-  Unit w;
-  if (a.req) {
-    if (!decode_unit_ragged(a, blockIdx.x, w)) return;  // past the batch's units (whole workgroup)
-  } else {
-    w = decode_unit(a, unit_of_block(a, blockIdx.x));
-  }
   const int P = w.P;
 
   const int r_blk = wave * 16 + ln;  // row within the block
@@ -331,8 +325,22 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs 
   }
 }
 
+// A uniform batch: one unit per workgroup.
+__global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_kernel(AttnArgs a) {
+  attn_mfma_f32_unit(a, decode_unit(a, unit_of_block(a, blockIdx.x)));
+}
+
+// A ragged batch: a persistent grid taking units from its XCD's counter.
+__global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_ragged_kernel(AttnArgs) {
+  for_each_ragged_unit([](const AttnArgs& a, const Unit& w) { attn_mfma_f32_unit(a, w); });
+}
+
 hipError_t launch_attn_mfma_f32(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  attn_mfma_f32_kernel<<<dim3(static_cast<unsigned>(plan.units)), kF32Threads, 0, stream>>>(a);
+  const dim3 grid(static_cast<unsigned>(plan.units));
+  if (a.req)
+    attn_mfma_f32_ragged_kernel<<<grid, kF32Threads, 0, stream>>>(a);
+  else
+    attn_mfma_f32_kernel<<<grid, kF32Threads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

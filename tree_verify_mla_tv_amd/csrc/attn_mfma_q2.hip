@@ -99,7 +99,7 @@ __device__ __forceinline__ float sum_row_lanes(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_q2_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_mfma_q2_unit(const AttnArgs& a, const Unit& w) {
   __shared__ int s_par[kMaxQ];
   __shared__ unsigned long long s_anc[kMaxQ * kAncWords];
   __shared__ float s_row_l[q2::kRows];
@@ -111,12 +111,6 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_q2_kernel(AttnArgs 
   const int g2 = lane >> 5;
   const int rho = lane >> 4;
   const int j = lane & 15;
-  Unit w;
-  if (a.req) {
-    if (!decode_unit_ragged(a, blockIdx.x, w)) return;  // past the batch's units (whole workgroup)
-  } else {
-    w = decode_unit(a, unit_of_block(a, blockIdx.x));
-  }
   const int P = w.P;
   TreeKv kv;
   kv.lat = raw_buffer(static_cast<const uint16_t*>(a.c_kv) + w.kv_row0 * mf::DC,
@@ -289,8 +283,22 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_q2_kernel(AttnArgs 
   }
 }
 
+// A uniform batch: one unit per workgroup.
+__global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_q2_kernel(AttnArgs a) {
+  attn_mfma_q2_unit(a, decode_unit(a, unit_of_block(a, blockIdx.x)));
+}
+
+// A ragged batch: a persistent grid taking units from its XCD's counter.
+__global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_q2_ragged_kernel(AttnArgs) {
+  for_each_ragged_unit([](const AttnArgs& a, const Unit& w) { attn_mfma_q2_unit(a, w); });
+}
+
 hipError_t launch_attn_mfma_q2(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  attn_mfma_q2_kernel<<<dim3(static_cast<unsigned>(plan.units)), kMfmaThreads, 0, stream>>>(a);
+  const dim3 grid(static_cast<unsigned>(plan.units));
+  if (a.req)
+    attn_mfma_q2_ragged_kernel<<<grid, kMfmaThreads, 0, stream>>>(a);
+  else
+    attn_mfma_q2_kernel<<<grid, kMfmaThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

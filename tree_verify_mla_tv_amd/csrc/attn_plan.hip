@@ -172,8 +172,7 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
   p.n_slots = 2 * p.target > cap ? 2 * p.target : cap;
   p.units = blocks + p.n_slots;
   p.merge_blocks = blocks < p.n_slots / 2 ? blocks : p.n_slots / 2;
-  const size_t rec = align256((merge_table_word0(s.B) + static_cast<size_t>(p.merge_blocks) * kMtFields) *
-                              sizeof(int32_t));
+  const size_t rec = align256((queue_word0(s.B, p.merge_blocks) + kXcdQueues) * sizeof(int32_t));
   p.ws_o_off = rec;
   p.ws_m_off = rec + align256(static_cast<size_t>(p.n_slots) * p.rows_per_block * s.d_c * sizeof(float));
   p.ws_l_off = p.ws_m_off + align256(static_cast<size_t>(p.n_slots) * p.rows_per_block * sizeof(float));
@@ -511,6 +510,8 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
     tot[kTotMerge] = tot_merge;
     tot[kTotChoice] = s_choice;
   }
+  // The persistent attention grid's per-XCD unit counters start at zero.
+  if (t < kXcdQueues) rq[queue_word0(B, max_merges) + t] = 0;
 }
 
 }  // namespace
@@ -655,10 +656,14 @@ __global__ __launch_bounds__(256) void attn_merge_ragged_kernel(AttnArgs a, int 
 }
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  hipError_t e = plan.kernel == AttnKernel::kMfmaBf16Q2 ? launch_attn_mfma_q2(s, plan, a, stream)
-                 : plan.kernel == AttnKernel::kMfmaBf16 ? launch_attn_mfma_bf16(s, plan, a, stream)
-                 : plan.kernel == AttnKernel::kMfmaF32  ? launch_attn_mfma_f32(s, plan, a, stream)
-                                                        : launch_attn_valu(s, plan, a, stream);
+  // A ragged batch runs a persistent grid (next_unit_ragged): as many
+  // workgroups as run at once, at most the bound of units.
+  AttnPlan lp = plan;
+  if (a.req) lp.units = plan.units < plan.target ? plan.units : plan.target;
+  hipError_t e = lp.kernel == AttnKernel::kMfmaBf16Q2 ? launch_attn_mfma_q2(s, lp, a, stream)
+                 : lp.kernel == AttnKernel::kMfmaBf16 ? launch_attn_mfma_bf16(s, lp, a, stream)
+                 : lp.kernel == AttnKernel::kMfmaF32  ? launch_attn_mfma_f32(s, lp, a, stream)
+                                                      : launch_attn_valu(s, lp, a, stream);
   if (e != hipSuccess || plan.merge_blocks == 0) return e;
   if (a.req) {
     // The tasks of the bound (merged blocks x tasks per block), at most 8

@@ -38,7 +38,7 @@ __device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
 }
 
 template <typename KV, int DC, int DR>
-__global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_valu_unit(const AttnArgs& a, const Unit& w) {
   constexpr int D = DC + DR;
   constexpr int S = D + 4;          // LDS row stride (floats): 16-byte rows, banks shift by 4 per row
   constexpr int C4 = D / 4;         // float4 chunks per row
@@ -56,12 +56,6 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   __shared__ unsigned long long s_anc[kMaxQ * kAncWords];
 
   const int tid = threadIdx.x;
-  Unit w;
-  if (a.req) {
-    if (!decode_unit_ragged(a, blockIdx.x, w)) return;  // past the batch's units (whole workgroup)
-  } else {
-    w = decode_unit(a, unit_of_block(a, blockIdx.x));
-  }
   const int r0 = w.rb * kValuRows;
   const int k_begin = w.k_begin;
   const int k_end = w.k_end;
@@ -207,13 +201,31 @@ __global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
   }
 }
 
+// A uniform batch: one unit per workgroup.
+template <typename KV, int DC, int DR>
+__global__ __launch_bounds__(kValuThreads) void attn_valu_kernel(AttnArgs a) {
+  attn_valu_unit<KV, DC, DR>(a, decode_unit(a, unit_of_block(a, blockIdx.x)));
+}
+
+// A ragged batch: a persistent grid taking units from its XCD's counter.
+template <typename KV, int DC, int DR>
+__global__ __launch_bounds__(kValuThreads) void attn_valu_ragged_kernel(AttnArgs) {
+  for_each_ragged_unit([](const AttnArgs& a, const Unit& w) { attn_valu_unit<KV, DC, DR>(a, w); });
+}
+
 template <typename KV, int DC>
 static hipError_t launch_valu_dr(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(plan.units));
-  if (s.d_r == 32)
+  if (a.req) {
+    if (s.d_r == 32)
+      attn_valu_ragged_kernel<KV, DC, 32><<<grid, kValuThreads, 0, stream>>>(a);
+    else
+      attn_valu_ragged_kernel<KV, DC, 64><<<grid, kValuThreads, 0, stream>>>(a);
+  } else if (s.d_r == 32) {
     attn_valu_kernel<KV, DC, 32><<<grid, kValuThreads, 0, stream>>>(a);
-  else
+  } else {
     attn_valu_kernel<KV, DC, 64><<<grid, kValuThreads, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

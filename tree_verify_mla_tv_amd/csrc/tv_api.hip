@@ -162,6 +162,7 @@ tv_status_t ragged_args(const float* q_lat, const float* q_rope, const void* c_k
   a.lse = lse;
   a.req = reinterpret_cast<const int32_t*>(ws);
   a.merge_tab = reinterpret_cast<const int4*>(ws + tv::merge_table_word0(B) * sizeof(int32_t));
+  a.queue = reinterpret_cast<int*>(ws + tv::queue_word0(B, plan.merge_blocks) * sizeof(int32_t));
   a.ws_o = reinterpret_cast<float*>(ws + plan.ws_o_off);
   a.ws_m = reinterpret_cast<float*>(ws + plan.ws_m_off);
   a.ws_l = reinterpret_cast<float*>(ws + plan.ws_l_off);

@@ -113,6 +113,7 @@ struct AttnArgs {
   const int4* merge_tab;  // the merge table after the records (MergeField order)
   int kv_stride;          // cache rows per request
   int n_nodes;            // rows of the caller's packed node arrays (the prep clamps the lengths to them)
+  int* queue;             // kXcds unit counters in the workspace (ragged batches; the prep kernel zeroes them)
 };
 
 // Records of a ragged batch, written by the prep kernel into the workspace
@@ -398,6 +399,52 @@ __host__ __device__ inline bool decode_unit_ragged(const AttnArgs& a, long long 
   w.par0 = r[kReqQStart];
   w.kv_row0 = static_cast<long long>(b) * a.kv_stride;
   return true;
+}
+
+// Ragged batches run a persistent grid: one workgroup per CU (two for the
+// vector kernel) takes launch slots from its XCD's counter, slot x = xcd + 8 j
+// for the j-th take on that XCD, so the units reaching each XCD are the ones a
+// grid of one workgroup per unit would deal it (runs of kDealGroup
+// neighbours sharing its L2), handed out as its CUs free up.  The counters sit
+// after the merge table in the workspace and the prep kernel zeroes them.
+// The grid (at least 256 workgroups) gives every counter workgroups.
+constexpr int kXcdQueues = 8;
+__host__ __device__ inline size_t queue_word0(int B, long long max_merges) {
+  return merge_table_word0(B) + static_cast<size_t>(max_merges) * kMtFields;
+}
+
+// Next unit of this workgroup in a ragged batch, or false when its XCD's
+// slots are used up (uniform across the workgroup).  The leading barrier
+// keeps the previous unit's LDS reads ahead of the next unit's writes; the
+// slot goes through readfirstlane so the unit's fields stay scalar.
+__device__ __forceinline__ bool next_unit_ragged(const AttnArgs& a, Unit& w) {
+  __shared__ int s_slot;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int k = static_cast<int>(blockIdx.x % kXcdQueues);
+    s_slot = k + kXcdQueues * atomicAdd(a.queue + k, 1);
+  }
+  __syncthreads();
+  return decode_unit_ragged(a, __builtin_amdgcn_readfirstlane(s_slot), w);
+}
+
+// The loop of a persistent ragged workgroup: body(a, w) for each unit it
+// takes.  The kernels using it take one argument, an AttnArgs by value, which
+// therefore starts the kernel-argument segment; the segment pointer passes
+// through an empty asm statement at each unit, so the compiler reloads the
+// arguments a unit needs where it needs them instead of holding every one in
+// registers across the whole loop (which spills).
+template <typename Body>
+__device__ __forceinline__ void for_each_ragged_unit(Body body) {
+  using KernArgs = const __attribute__((address_space(4))) AttnArgs*;
+  KernArgs pa = (KernArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  Unit w;
+  for (;;) {
+    asm volatile("" : "+s"(pa));
+    const AttnArgs& a = *(const AttnArgs*)pa;
+    if (!next_unit_ragged(a, w)) return;
+    body(a, w);
+  }
 }
 
 hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
