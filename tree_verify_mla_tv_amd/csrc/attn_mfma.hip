@@ -315,17 +315,11 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_kernel(AttnArg
   attn_mfma_bf16_unit(a, decode_unit(a, unit_of_block(a, blockIdx.x)));
 }
 
-// A ragged batch: a persistent grid taking units from its XCD's counter.
-__global__ __launch_bounds__(kMfmaThreads, 1) void attn_mfma_bf16_ragged_kernel(AttnArgs) {
-  for_each_ragged_unit([](const AttnArgs& a, const Unit& w) { attn_mfma_bf16_unit(a, w); });
-}
-
 hipError_t launch_attn_mfma_bf16(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(plan.units));
-  if (a.req)
-    attn_mfma_bf16_ragged_kernel<<<grid, kMfmaThreads, 0, stream>>>(a);
-  else
-    attn_mfma_bf16_kernel<<<grid, kMfmaThreads, 0, stream>>>(a);
+  // Ragged batches always run the two-term kernel (their entry points take no
+  // query-precision option).
+  if (a.req) return hipErrorNotSupported;
+  attn_mfma_bf16_kernel<<<dim3(static_cast<unsigned>(plan.units)), kMfmaThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
