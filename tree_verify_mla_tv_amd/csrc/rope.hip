@@ -108,7 +108,6 @@ __global__ __launch_bounds__(kRopeThreads) void tree_rope_kernel(float* __restri
                                                                  int npb, RopeFreq f,
                                                                  const int32_t* __restrict__ req) {
   __shared__ int s_parent[kMaxQ];
-  __shared__ int s_depth[kRopeMaxNodes];
   __shared__ double s_cs[kRopeMaxNodes][kMaxHalf][2];
   const int b = blockIdx.y;
   const int i0 = blockIdx.x * npb;
@@ -151,22 +150,20 @@ __global__ __launch_bounds__(kRopeThreads) void tree_rope_kernel(float* __restri
   }
 
 
-  // Depths (ancestors have lower indices: parents are clamped) and angles.
+  // Depths (ancestors have lower indices: parents are clamped) and angles:
+  // each angle's thread walks its node's chain itself (the chain is short and
+  // in LDS; one barrier fewer than a shared depth table).
   s_parent[t] = t < i_end ? clamp_parent(par, t) : -1;  // unconditional: the load stays where it is
-  __syncthreads();
-  if (t < nn) {
-    int d = 0;
-    for (int n = s_parent[i0 + t]; n >= 0; n = s_parent[n]) ++d;
-    s_depth[t] = d;
-  }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int j = t + r * kRopeThreads;
     if (j < n_ang) {
       const int n = j / half, k = j - n * half;
+      int d = 0;
+      for (int m = s_parent[i0 + n]; m >= 0; m = s_parent[m]) ++d;
       double sn, cs;
-      sincos(static_cast<double>(prefix_len + s_depth[n]) * (r == 0 ? fr0 : fr1), &sn, &cs);
+      sincos(static_cast<double>(prefix_len + d) * (r == 0 ? fr0 : fr1), &sn, &cs);
       s_cs[n][k][0] = cs;
       s_cs[n][k][1] = sn;
     }
