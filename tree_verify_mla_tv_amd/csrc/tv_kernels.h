@@ -113,7 +113,7 @@ struct AttnArgs {
   const int4* merge_tab;  // the merge table after the records (MergeField order)
   int kv_stride;          // cache rows per request
   int n_nodes;            // rows of the caller's packed node arrays (the prep clamps the lengths to them)
-  int* queue;             // kXcds unit counters in the workspace (ragged batches; the prep kernel zeroes them)
+  int* queue;             // kXcdQueues unit counters in the workspace (ragged batches; the prep kernel zeroes them)
 };
 
 // Records of a ragged batch, written by the prep kernel into the workspace
