@@ -137,9 +137,11 @@ def copy_calibration(torch) -> int:
     return 0
 
 
-def _time_ms(torch, fn, reps: int) -> float:
-    """Mean ms per call over reps calls, HIP events on the current stream."""
-    fn()
+def _time_ms(torch, fn, reps: int, warmup: int = 1) -> float:
+    """Mean ms per call over reps calls after warmup untimed ones, HIP events
+    on the current stream."""
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -356,7 +358,7 @@ def verify_variants(torch, tv, W) -> dict:
         o = torch.empty_like(q_lat)
         ws = torch.empty(max(tv.workspace_size(B, H, q, P, d_c, d_r, tv.TV_BF16), 1), dtype=torch.uint8, device=dev)
         ms = _time_ms(torch, lambda: tv.verify_attn(q_lat, q_rope, c_kv, k_rope, parent, P, sm, out=o, workspace=ws),
-                      10)
+                      20, warmup=5)
         flops = H * sum(visible_pairs(par[b], P) for b in range(B)) * (2 * (d_c + d_r) + 2 * d_c)
         out[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
         del q_lat, q_rope, c_kv, k_rope, o, ws
@@ -375,7 +377,7 @@ def verify_variants(torch, tv, W) -> dict:
     ws = torch.empty(tv.load().tv_verify_attn_ragged_workspace_size(B, H, max(q_lens), S, d_c, d_r, tv.TV_BF16),
                      dtype=torch.uint8, device=dev)
     ms = _time_ms(torch, lambda: tv.verify_attn_ragged(q_lat, q_rope, c_kv, k_rope, parent, pl, ql, max(q_lens), sm,
-                                                       out=o, workspace=ws), 10)
+                                                       out=o, workspace=ws), 20, warmup=5)
     flops = H * sum(visible_pairs(p_, P) for p_, P in zip(pars, prefixes)) * (2 * (d_c + d_r) + 2 * d_c)
     out["ragged_b32_q9to33_p2kto16k"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
     return out
