@@ -133,14 +133,18 @@ tv_status_t tv_rope_neox_strided(void* x, tv_dtype_t dtype, const int32_t* pos, 
  *   kv_dtype TV_F32 or TV_BF16.  1 <= q_len <= TV_MAX_Q_LEN.  One tree's
  *   latent rows (kv_len * d_c elements of kv_dtype) must stay below 2^31
  *   bytes (TV_ERR_UNSUPPORTED otherwise).
- *   Arithmetic: with a bf16 cache at (512, 64) both contractions run on bf16
- *   matrix cores: each scaled query x = sm_scale * log2(e) * q (rounded to
- *   fp32) enters as two bf16 terms, hi = bf16(x) and lo = bf16(x - hi), so
- *   the scores are those of the fp32 queries to fp32 accumulation; the
- *   softmax weights are rounded to bf16 for the value product (fp32
- *   accumulation, row sums of the rounded weights).  With an fp32 cache at
- *   (512, 64) on fp32 matrix cores; other shapes on the fp32 vector ALU.  The
- *   sums run in a different order than the plain definition.
+ *   Arithmetic: with a bf16 cache at (512, 64) both contractions run on
+ *   16-bit matrix cores.  Scores: each scaled query x = sm_scale * log2(e) * q
+ *   (rounded to fp32) enters as two bf16 terms, hi = bf16(x) and
+ *   lo = bf16(x - hi), so the scores are those of the fp32 queries to fp32
+ *   accumulation.  Values: the softmax weights are rounded to fp16, and the
+ *   latent rows are converted from bf16 to fp16, exactly for values below
+ *   65504 in magnitude (fp32 accumulation, row sums of the rounded weights).
+ *   Latent cache values of magnitude 65504 or more are outside this path's
+ *   range and give non-finite outputs (use an fp32 cache for such data).
+ *   With an fp32 cache at (512, 64) on fp32 matrix cores; other shapes on the
+ *   fp32 vector ALU.  The sums run in a different order than the plain
+ *   definition.
  *   workspace: caller-owned device scratch of at least
  *   tv_verify_attn_workspace_size(...) bytes (NULL allowed when that is 0).
  *   out must not overlap any input.
@@ -174,10 +178,12 @@ tv_status_t tv_verify_attn_noalloc(const float* q_lat, const float* q_rope, cons
  * tv_verify_attn_ex — tv_verify_attn with option flags (0 gives tv_verify_attn
  *   exactly).  [Verify page, as for tv_verify_attn]
  *   TV_ATTN_BF16_QUERIES: with a bf16 cache at (512, 64), round each scaled
- *   query to ONE bf16 term (a single score pass over twice the rows per
- *   workgroup: faster, but every score moves by up to 2^-9 of its terms;
- *   right when the queries are bf16 values already, or when that error is
- *   acceptable).  No effect on other shapes.  Unknown flag bits return
+ *   query to ONE bf16 term and the softmax weights to bf16, with the values
+ *   in bf16 (a single score pass over twice the rows per workgroup: faster,
+ *   and no range limit on the latent cache, but every score moves by up to
+ *   2^-9 of its terms and every weight by 2^-9; right when the queries are
+ *   bf16 values already, or when that error is acceptable).  No effect on
+ *   other shapes.  Unknown flag bits return
  *   TV_ERR_INVALID.  The workspace must hold
  *   tv_verify_attn_ex_workspace_size(..., flags) bytes.
  */

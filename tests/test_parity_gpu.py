@@ -20,16 +20,11 @@ import torch
 from oracle import tv_oracle as O
 from tree_verify_mla_tv_amd import tv
 from tree_verify_mla_tv_amd import workloads as W
-from tvcompare import errors, pass_line, rope_mismatch
+from tvcompare import errors, lse_bound, pass_line, rope_mismatch
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": dict(max_abs=1e-5, max_rel=1e-2), "bf16": dict(max_rel=2e-2)}
-# lse: the fp32 paths round scores at ~1e-7 relative.  The bf16 path rounds the
-# softmax weights to bf16 (each within 2^-9 relative, so the log of their sum
-# moves by at most ~2^-9) and the scaled queries to bf16 (each score moves by a
-# few 2^-9 of its terms); the allowance is 2^-8 plus 2^-12 of |lse|.
-LSE_TOL = {"f32": lambda r: 2e-5, "bf16": lambda r: 2.0 ** -8 + 2.0 ** -12 * np.abs(r)}
+TOL = {"f32": dict(max_abs=1e-5, max_rel=1e-2), "bf16": dict(max_rel=2e-2), "bf16_queries": dict(max_rel=2e-2)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -65,7 +60,7 @@ def check_out(tag, shape, out, lse, ref_out, ref_lse, dtype, rows=None):
     if "max_abs" in tol:
         assert e["max_abs"] <= tol["max_abs"], (tag, e)
     el = float(np.max(np.abs(lse - ref_lse)))
-    assert np.all(np.abs(lse - ref_lse) <= LSE_TOL[dtype](ref_lse)), (tag, "lse", el)
+    assert np.all(np.abs(lse - ref_lse) <= lse_bound(dtype, ref_lse)), (tag, "lse", el)
     print(pass_line(tag, shape, e) + f" lse_abs={el:.1e}", flush=True)
     return e
 
@@ -266,29 +261,62 @@ def test_constant_latent_and_root_copy(dt):
     assert np.max(np.abs(out1 - 1.0)) <= 4 * 2.0 ** -23
 
 
-def test_bf16_late_large_scores_resweep():
-    """Scores that rise far above the first tile's max (more than 2^64 in the
-    base-2 weights) must still give the softmax of the oracle."""
+def test_bf16_cache_value_range():
+    """The default bf16-cache kernel converts the latent (value) rows to fp16:
+    exact for every bf16 value below 65504 in magnitude.  Latent values with
+    magnitudes spread over 2^-24 .. 2^15.5 (both signs; small queries keep the
+    scores moderate) must still give the oracle's output."""
+    rng = np.random.default_rng(17)
+    B, H, q, P, d_c, d_r = 2, 8, 9, 700, 512, 64
+    kv = P + q
+    mag = np.exp2(rng.uniform(-24.0, 15.5, (B, kv, d_c)))
+    c_kv32 = (mag * np.where(rng.random((B, kv, d_c)) < 0.5, -1.0, 1.0)).astype(np.float32)
+    c_kv = W.f32_to_bf16_bits(c_kv32)
+    k_rope = W.f32_to_bf16_bits((rng.standard_normal((B, kv, d_r)) * 0.5).astype(np.float32))
+    q_lat = (rng.standard_normal((B, q, H, d_c)) * 2e-5).astype(np.float32)
+    q_rope = (rng.standard_normal((B, q, H, d_r)) * 0.5).astype(np.float32)
+    parent = np.stack([W.tree_branch(q, rng) for _ in range(B)]).astype(np.int32)
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, "bf16"),
+                                     O.as_f64(k_rope, "bf16"), parent, P, sm)
+    out, lse = tv.verify_attn(cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, "bf16"), cuda_cache(k_rope, "bf16"),
+                              torch.from_numpy(parent).cuda(), P, sm, return_lse=True)
+    torch.cuda.synchronize()
+    check_out("bf16 latent values 2^-24..2^15.5", "B2 H8 q9 P700", out, lse, ref_out, ref_lse, "bf16")
+
+
+@pytest.mark.parametrize("rise", [30.0, 100.0])
+def test_bf16_late_large_scores_resweep(rise):
+    """Scores that rise far above the first tile's max must still give the
+    softmax of the oracle: by ~rise log2 units, past the default kernel's
+    fp16-weight headroom (2^15) at 30, past the one-term option's (2^64) at
+    100; both kernels."""
     rng = np.random.default_rng(91)
     B, H, q, P, d_c, d_r = 1, 4, 3, 300, 512, 64
     kv = P + q
     u = (rng.standard_normal(d_c) * 0.5).astype(np.float32)
     q_lat = np.broadcast_to(u, (B, q, H, d_c)).astype(np.float32).copy()
     q_rope = np.zeros((B, q, H, d_r), np.float32)
+    sm = 0.25
+    base = rise / (sm * float(u.astype(np.float64) @ u) * np.log2(np.e))
     t = np.zeros(kv, np.float32)
-    t[64:] = 2.5 + 0.5 * rng.random(kv - 64).astype(np.float32)
+    t[64:] = base * (1.0 + 0.2 * rng.random(kv - 64)).astype(np.float32)
     c_kv32 = (t[:, None] * u[None, :])[None].astype(np.float32)
     c_kv = W.f32_to_bf16_bits(c_kv32)
     k_rope = W.f32_to_bf16_bits(np.zeros((B, kv, d_r), np.float32))
     parent = W.tree_chain(q)[None].astype(np.int32)
-    sm = 0.25
     ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, "bf16"),
                                      O.as_f64(k_rope, "bf16"), parent, P, sm)
-    assert ref_lse.min() > 64.0 * np.log(2.0)  # far above the first tile's max of 0
-    out, lse = tv.verify_attn(cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, "bf16"),
-                              cuda_cache(k_rope, "bf16"), torch.from_numpy(parent).cuda(), P, sm, return_lse=True)
+    assert ref_lse.min() > (rise - 1.0) * np.log(2.0)  # far above the first tile's max of 0
+    args = (cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, "bf16"), cuda_cache(k_rope, "bf16"),
+            torch.from_numpy(parent).cuda(), P, sm)
+    out, lse = tv.verify_attn(*args, return_lse=True)
     torch.cuda.synchronize()
-    check_out("late-large-scores", "B1 H4 q3 P300", out, lse, ref_out, ref_lse, "bf16")
+    check_out(f"late-large-scores rise {rise:g}", "B1 H4 q3 P300", out, lse, ref_out, ref_lse, "bf16")
+    out, lse = tv.verify_attn_ex(*args, tv.TV_ATTN_BF16_QUERIES, return_lse=True)
+    torch.cuda.synchronize()
+    check_out(f"late-large-scores rise {rise:g} bf16 queries", "B1 H4 q3 P300", out, lse, ref_out, ref_lse,
+              "bf16_queries")
 
 
 # The three attention kernels: (d_c, d_r, cache dtype) that selects each.
@@ -449,7 +477,7 @@ def test_bf16_queries_edge_shapes(case):
     out, lse = tv.verify_attn_ex(cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, dt), cuda_cache(k_rope, dt),
                                  torch.from_numpy(parent).cuda(), P, sm, tv.TV_ATTN_BF16_QUERIES, return_lse=True)
     torch.cuda.synchronize()
-    check_out("edge bf16 queries", str(case), out, lse, ref_out, ref_lse, dt)
+    check_out("edge bf16 queries", str(case), out, lse, ref_out, ref_lse, "bf16_queries")
 
 
 def test_bf16_queries_serving_scale():
@@ -467,7 +495,7 @@ def test_bf16_queries_serving_scale():
     out, lse = tv.verify_attn_ex(q_lat, q_rope, c_kv, k_rope, parent, w.prefix_len, w.sm_scale,
                                  tv.TV_ATTN_BF16_QUERIES, return_lse=True)
     torch.cuda.synchronize()
-    check_out(w.name + " bf16 queries", w.describe(), out, lse, ref["out"], ref["lse"], "bf16")
+    check_out(w.name + " bf16 queries", w.describe(), out, lse, ref["out"], ref["lse"], "bf16_queries")
 
 
 @pytest.mark.parametrize("d_r,H,dt", [(6, 3, "f32"), (32, 8, "bf16"), (64, 64, "bf16"), (128, 1, "f32"),

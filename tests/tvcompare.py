@@ -75,3 +75,21 @@ def rope_mismatch(got, ref, x_raw, dtype: str, max_pos: int):
     d = np.abs(g - r)
     beyond = int(np.count_nonzero(d > ulp + pair * (max_pos + 4) * 2.0 ** -50))
     return beyond, float(np.count_nonzero(d) / d.size)
+
+
+def lse_bound(kind, ref_lse):
+    """Allowed |lse - ref| per row.  f32: scores rounded at ~1e-7 relative.
+    bf16 (the default bf16-cache kernel): scores to fp32 precision, softmax
+    weights rounded to fp16 (each within 2^-11 relative, so the log of their
+    sum moves by at most ~2^-11): 2^-10 plus 2^-14 of |lse|.  bf16_queries (the
+    one-term option): weights rounded to bf16 (2^-8) and each score moved by a
+    few 2^-9 of its terms: 2^-8 plus 2^-12 of |lse|."""
+    r = np.abs(np.asarray(ref_lse, np.float64))
+    if kind == "f32":
+        return np.full_like(r, 2e-5)
+    if kind == "bf16":
+        return 2.0 ** -10 + 2.0 ** -14 * r
+    if kind == "bf16_queries":
+        return 2.0 ** -8 + 2.0 ** -12 * r
+    raise ValueError(kind)
+

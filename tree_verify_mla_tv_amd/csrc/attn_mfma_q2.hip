@@ -11,8 +11,14 @@
 // dominant latent channels (structured activations rather than i.i.d. draws)
 // shifts near-one-hot weights far past the bf16-cache tolerance.  This kernel
 // carries each scaled query x as hi = bf16(x) plus lo = bf16(x - hi) (x to
-// 2^-17), so the scores are those of the fp32 queries up to fp32 accumulation;
-// the softmax weights are still rounded to bf16 for the value product.
+// 2^-17), so the scores are those of the fp32 queries up to fp32 accumulation.
+// The value product runs in fp16: the softmax weights are rounded to fp16
+// (2^-11, where bf16 would give 2^-8), and each bf16 latent row is converted
+// to fp16 in registers, exactly for cache values below 65504 in magnitude
+// (bf16 carries 8 significant bits, fp16 11; values under 2^-14 become fp16
+// subnormals, 2^-24 apart).  fp16 weights bound the reference-max headroom:
+// a weight exp2(s - m_ref) must stay below 65504, so a tile whose scores pass
+// m_ref by more than kHeadroom triggers the re-sweep.
 //
 // Workgroup = 4 waves (one per SIMD), 64 query rows of one tree.  Wave w owns
 // rows 16 w .. 16 w + 15 for the scores: the B operand of its score product
@@ -32,14 +38,15 @@ namespace tv {
 
 namespace q2 {
 constexpr int kRows = kQ2Rows;                      // 64 query rows per workgroup
-constexpr int kPBytes = kRows * kMfmaKeys * 2;      // 4096: one tile's bf16 weights
+constexpr int kPBytes = kRows * kMfmaKeys * 2;      // 4096: one tile's fp16 weights
+constexpr float kHeadroom = 15.0f;                  // log2 units above m_ref: weights below 2^15 fit fp16
 }  // namespace q2
 
 // Three kv tile buffers in rotation (layout of attn_mfma_common.h).
 __shared__ __align__(16) unsigned char g_q2_k0[mf::kBufBytes];
 __shared__ __align__(16) unsigned char g_q2_k1[mf::kBufBytes];
 __shared__ __align__(16) unsigned char g_q2_k2[mf::kBufBytes];
-// Softmax weights of two consecutive tiles, [rb][key half h][lane][8 x bf16]:
+// Softmax weights of two consecutive tiles, [rb][key half h][lane][8 x fp16]:
 // lane L holds row 32 rb + L % 32 and keys 16 h + {4 G .. 4 G + 3, 8 + 4 G ..
 // 8 + 4 G + 3} (G = L / 32) -- the B operand of the value product.
 __shared__ __align__(16) unsigned char g_q2_p[2][q2::kPBytes];
@@ -222,7 +229,7 @@ __device__ __forceinline__ void attn_mfma_q2_unit(const AttnArgs& a, const Unit&
       kn = nx;
     }
     asm volatile("s_waitcnt vmcnt(0)\n" TV_MFMA_DRAIN_ASM ::: "memory");
-    const bool over = st.exc > mf::kHeadroom;
+    const bool over = st.exc > q2::kHeadroom;
     if (threadIdx.x == 0) s_redo = 0;
     __syncthreads();
     if (__any(over) && lane == 0) s_redo = 1;

@@ -18,12 +18,17 @@ TV_Q2_STEP_ASM -- per wave, for tile t (scores) and tile t-1 (values):
      for keys 8 (i/4) + 4 (l/32) + i % 4 in score i.
      Woven in: this wave's copy of tile t+1 (the TV_STAGE_ASM loads of
      attn_mfma_asm.h, one group per op) and the LDS reads of the value
-     fragments of tile t-1, read well ahead into the AGPR pool.
+     fragments of tile t-1, read well ahead: the weights into the AGPR pool,
+     the latent (value) fragments into v[192:223], fragment f at
+     v[192 + 4 f], and there converted from bf16 to fp16 in place, CVT_DELAY
+     matrix ops after their read (per dword: widen both halves to fp32, then
+     one v_cvt_pk_f16_f32; exact below 65504 in magnitude).
   2. Values O^T[rb][db] (%[o<4 rb + db>], rb = 0, 1: rows 32 rb .. 32 rb + 31)
-     += V(db, h) x P(rb, h): 16 ops, n = 8 h + 2 db + rb.  V(db, h) is read
-     from the row-major tile with two ds_read_b64_tr_b16 at %[tb] + 16640 h +
-     16 db (+ 8320 for keys 8..15 of the half), P(rb, h) with ds_read_b128 at
-     %[pb] + 1024 (2 rb + h).
+     += V(db, h) x P(rb, h): 16 x v_mfma_f32_32x32x16_f16, n = 8 h + 2 db + rb.
+     V(db, h) (fragment f = 2 h ... as n >> 1) is read from the row-major
+     tile with two ds_read_b64_tr_b16 at %[tb] + 16640 h + 16 db (+ 8320 for
+     keys 8..15 of the half), P(rb, h) with ds_read_b128 at %[pb] + 1024
+     (2 rb + h).
      Woven in, for tile t (VALU):
        combine  v_permlane16_swap of scores i and i + 8, then their sum: lane
                 l (row l % 16, rho = l / 16) keeps 8 scores, of keys
@@ -34,39 +39,43 @@ TV_Q2_STEP_ASM -- per wave, for tile t (scores) and tile t-1 (values):
                 l ^ 32, l ^ 48: v_permlane16_swap and v_permlane32_swap);
        state    %[mseen], %[mref] (set on the first visible tile), %[exc],
                 reference max(%[mref], -FLT_MAX), as in attn_mfma.hip;
-       weights  exp2(s - ref), packed to bf16 in v[240:243] and stored with
+       weights  exp2(s - ref), packed to fp16 in v[240:243] and stored with
                 one ds_write_b128 at %[pw] (the B operand of the value product
                 for the lane's row block, key half and key group);
-       row sum  %[l] adds the packed (rounded) weights, unpacked by a shift
-                and a mask.
+       row sum  %[l] adds the packed (rounded) weights, widened back to fp32.
      These ops are list-scheduled into the gaps after value ops (dependencies
      from their register operands; plain VALU results are forwarded, so a
      consumer may share its producer's gap unless the producer is a
      transcendental or the consumer a v_permlane*_swap; the mask is a
      pseudo-op between the combine and everything after it).
-All LDS fragments of the matrix ops go through a pool of 32 AGPR quads
-a[128:255]; a quad is reused one matrix op after its last reader.  Waits are
-exact lgkmcnt counts from the wave's in-order LDS queue.
+The K and weight fragments of the matrix ops go through a pool of 32 AGPR
+quads a[128:255]; a quad is reused one matrix op after its last reader.  Waits
+are exact lgkmcnt counts from the wave's in-order LDS queue.
 
 Hazards handled: LDS data waits; the matrix result S before its first VALU
 read (>= S_HAZARD wait states); the copy's M0 and offset writes a matrix op
 before the loads that read them; v_permlane*_swap two wait states after the
 VALU write of a source and a transcendental's result one wait state before
 its first reader (both kept a matrix op apart, or by s_nop in the last gap);
+a converted value fragment at least one matrix op before its first reader;
 the accumulators before anything outside the sweep
 reads them (TV_MFMA_DRAIN_ASM of attn_mfma_asm.h after the last step).
 """
 import os
+import re
 
 import gen_mfma_asm as G
 
 S_BASE = 224                                  # v[224:239]: scores
 P_PACK = 240                                  # v[240:243]: packed weights
 TMP = list(range(244, 252))                   # v[244:251]: VALU temporaries
-CLOBBERED_V = list(range(S_BASE, 252))
+V_BASE = 192                                  # v[192:223]: value fragments V0..V7, four dwords each
+CVT_TMP = 190                                 # v190: temporary of the bf16 -> fp16 conversion
+CLOBBERED_V = list(range(CVT_TMP, 224)) + list(range(S_BASE, 252))
 POOL = [128 + 4 * i for i in range(32)]       # a[128:255]: LDS fragment quads
 AHEAD_K = 8           # a K fragment is read at most this many matrix ops before its use
 AHEAD_VP = 24         # value-phase fragments may be read this far ahead (during the scores)
+CVT_DELAY = 6         # a value fragment is converted this many matrix ops after its read
 LOADS_PER_GAP = 2     # LDS fragment reads issued before one matrix op, at most
 COPY_GROUPS = 18      # copy groups, one after each of the first score ops
 GAP_BUDGET = 6        # VALU instructions between two value ops
@@ -88,6 +97,7 @@ def aquad(r):
 
 def rw(text):
     """(registers read, registers written) of one VALU / LDS-store op."""
+    text = re.sub(r"\s+src0_sel:\S+", "", text)
     if text.startswith("v_permlane16_swap") or text.startswith("v_permlane32_swap"):
         _, _, rest = text.partition(" ")
         regs = [G._regs(o) for o in rest.split(",")]
@@ -154,14 +164,14 @@ def softmax_valu():
         op(f"v_exp_f32 {S(i)}, {S(i)}")
     pk = [f"v{P_PACK + k}" for k in range(4)]
     for k in range(4):
-        op(f"v_cvt_pk_bf16_f32 {pk[k]}, {S(2 * k)}, {S(2 * k + 1)}")
+        op(f"v_cvt_pk_f16_f32 {pk[k]}, {S(2 * k)}, {S(2 * k + 1)}")
     op(f"ds_write_b128 %[pw], v[{P_PACK}:{P_PACK + 3}]", lds="w")
     op(f"v_mov_b32 {t[4]}, 0")
     for k in range(4):
         acc = "%[l]" if k % 2 == 0 else t[4]
         lo, hi = (t[5], t[6]) if k % 2 == 0 else (t[7], t[1])
-        op(f"v_lshlrev_b32 {lo}, 16, {pk[k]}")
-        op(f"v_and_b32 {hi}, 0xffff0000, {pk[k]}")
+        op(f"v_cvt_f32_f16 {lo}, {pk[k]}")
+        op(f"v_cvt_f32_f16_sdwa {hi}, {pk[k]} src0_sel:WORD_1")
         op(f"v_add_f32 {acc}, {acc}, {lo}")
         op(f"v_add_f32 {acc}, {acc}, {hi}")
     op(f"v_add_f32 %[l], %[l], {t[4]}")
@@ -211,17 +221,18 @@ def step_asm() -> str:
     pending = list(order)
     for m in range(len(mfma)):
         for fr in release.get(m, []):
-            free.append(where[fr])
+            if fr[0] != "V":
+                free.append(where[fr])
         issued = 0
         for fr in list(pending):
-            if not free:
-                break
+            if not free and fr[0] != "V":
+                continue
             must = first_use[fr] <= m
             # before the first op, every K fragment within reach (the step
             # starts with the pipeline of reads empty)
             cap = AHEAD_K + 1 if m == 0 else LOADS_PER_GAP
             if first_use[fr] <= m + ahead(fr) and (issued < cap or must):
-                where[fr] = free.pop(0)
+                where[fr] = V_BASE + 4 * int(fr[1:]) if fr[0] == "V" else free.pop(0)
                 loads_before[m].append(fr)
                 pending.remove(fr)
                 issued += 1
@@ -230,6 +241,8 @@ def step_asm() -> str:
 
     lines = ["s_mov_b32 %[ms], m0"]
     q = G.LdsQueue(lines)
+    cur_m = [0]
+    read_at = {}
     ws = [None]   # wait states since the last score op
 
     def emit(text, lds_name=None):
@@ -251,8 +264,9 @@ def step_asm() -> str:
         elif kind == "V":
             f = int(idx)
             off = 16640 * (f >> 2) + 16 * (f & 3)
-            emit(f"ds_read_b64_tr_b16 a[{r}:{r + 1}], %[tb] offset:{off}", fr + "lo")
-            emit(f"ds_read_b64_tr_b16 a[{r + 2}:{r + 3}], %[tb] offset:{off + 8320}", fr)
+            emit(f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[tb] offset:{off}", fr + "lo")
+            emit(f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[tb] offset:{off + 8320}", fr)
+            read_at[f] = cur_m[0]
         else:  # P<rb><h>
             rb, h = int(idx[0]), int(idx[1])
             emit(f"ds_read_b128 {aquad(r)}, %[pb] offset:{1024 * (2 * rb + h)}", fr)
@@ -315,10 +329,40 @@ def step_asm() -> str:
             placed += need
             trans += is_trans
 
+    def convert_half(f, h):
+        """bf16 -> fp16 in place, dwords 2h, 2h + 1 of value fragment f
+        (exact: every bf16 cache value below 65504 in magnitude is an fp16
+        value, subnormal ones rounded to fp16's 2^-24 spacing)."""
+        base = V_BASE + 4 * f
+        for d in (base + 2 * h, base + 2 * h + 1):
+            emit(f"v_lshlrev_b32 v{CVT_TMP}, 16, v{d}")
+            emit(f"v_and_b32 v{d}, 0xffff0000, v{d}")
+            emit(f"v_cvt_pk_f16_f32 v{d}, v{CVT_TMP}, v{d}")
+
+    cvt_todo = []      # (fragment, half) in order; one half per gap once due
+    cvt_done_at = {}   # fragment -> matrix-op index after which it was converted
+
+    def convert_due(m):
+        if cvt_todo:
+            f, h = cvt_todo[0]
+            if read_at[f] + CVT_DELAY <= m or first_use[f"V{f}"] <= m + 2:
+                cvt_todo.pop(0)
+                if h == 0:
+                    q.wait_for(f"V{f}")
+                convert_half(f, h)
+                if h == 1:
+                    cvt_done_at[f] = m
+
     for m, (kind, idx) in enumerate(mfma):
+        cur_m[0] = m
         for fr in loads_before[m]:
             load(fr)
+            if fr[0] == "V":
+                cvt_todo.extend([(int(fr[1:]), 0), (int(fr[1:]), 1)])
         q.wait_for(*needs[m])
+        if kind == "pv":
+            f_need = idx >> 1
+            assert cvt_done_at.get(f_need, m) < m - 1, f"value fragment {f_need} converted too late for op {m}"
         if kind == "qk":
             ks = idx
             b = f"%[q{ks}]" if ks < 32 else f"%[qr{ks - 32}]"
@@ -327,17 +371,21 @@ def step_asm() -> str:
             if ks < len(stage):
                 for x in stage[ks]:
                     emit(x)
+            convert_due(m)
             if ks == 35:
                 ws[0] = 0
         else:
             n = idx
             f, rb = n >> 1, n & 1
             o = f"%[o{4 * rb + (f & 3)}]"
-            emit(f"v_mfma_f32_32x32x16_bf16 {o}, {aquad(where[f'V{f}'])}, {aquad(where[f'P{rb}{f >> 2}'])}, {o}")
+            vq = where[f"V{f}"]
+            emit(f"v_mfma_f32_32x32x16_f16 {o}, v[{vq}:{vq + 3}], {aquad(where[f'P{rb}{f >> 2}'])}, {o}")
+            convert_due(m)
             fill_gap(n, GAP_BUDGET, n == 15)
             if n == 0:
                 assert first_read[0], "the first gap must start the softmax"
     assert not pending_v, "softmax does not fit between the value ops"
+    assert not cvt_todo and len(cvt_done_at) == 8, "value fragments left unconverted"
     lines.append("s_mov_b32 m0, %[ms]")
     lines.append("s_waitcnt lgkmcnt(0)")
     lines.append("s_branch .Ltv_q2_end_%=")
