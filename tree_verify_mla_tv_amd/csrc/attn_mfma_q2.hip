@@ -28,9 +28,9 @@
 // 32-row block with bf16 queries, for half the rows).  Every wave accumulates
 // output columns 128 w .. 128 w + 127 of all 64 rows (O^T = V^T P^T, two row
 // blocks of 32, 8 x 16 fp32 accumulators per lane).  The sweep, the copy of
-// the kv tiles, the softmax against a reference max and the re-sweep past 2^64
-// headroom are those of attn_mfma.hip; one step is one barrier and one
-// generated asm block (TV_Q2_STEP_ASM, gen_mfma_q2_asm.py).
+// the kv tiles, the softmax against a reference max and the re-sweep are those
+// of attn_mfma.hip (the headroom here 2^15, for the fp16 weights); one step is
+// one barrier and one generated asm block (TV_Q2_STEP_ASM, gen_mfma_q2_asm.py).
 #include "attn_mfma_common.h"
 #include "attn_mfma_q2_asm.h"
 
