@@ -138,10 +138,11 @@ tv_status_t tv_rope_neox_strided(void* x, tv_dtype_t dtype, const int32_t* pos, 
  *   (rounded to fp32) enters as two bf16 terms, hi = bf16(x) and
  *   lo = bf16(x - hi), so the scores are those of the fp32 queries to fp32
  *   accumulation.  Values: the softmax weights are rounded to fp16, and the
- *   latent rows are converted from bf16 to fp16, exactly for values below
- *   65504 in magnitude (fp32 accumulation, row sums of the rounded weights).
- *   Latent cache values of magnitude 65504 or more are outside this path's
- *   range and give non-finite outputs (use an fp32 cache for such data).
+ *   latent rows are converted from bf16 to fp16: exactly for magnitudes from
+ *   2^-17 to 65504, smaller ones rounded to fp16's 2^-24 spacing (fp32
+ *   accumulation, row sums of the rounded weights).  Latent cache values of
+ *   magnitude 65520 or more are outside this path's range and give
+ *   non-finite outputs (use an fp32 cache for such data).
  *   With an fp32 cache at (512, 64) on fp32 matrix cores; other shapes on the
  *   fp32 vector ALU.  The sums run in a different order than the plain
  *   definition.

@@ -263,7 +263,8 @@ def test_constant_latent_and_root_copy(dt):
 
 def test_bf16_cache_value_range():
     """The default bf16-cache kernel converts the latent (value) rows to fp16:
-    exact for every bf16 value below 65504 in magnitude.  Latent values with
+    exact for magnitudes from 2^-17 to 65504 (smaller ones rounded to fp16's
+    2^-24 spacing, at most 2^-25 off).  Latent values with
     magnitudes spread over 2^-24 .. 2^15.5 (both signs; small queries keep the
     scores moderate) must still give the oracle's output."""
     rng = np.random.default_rng(17)

@@ -14,9 +14,10 @@
 // 2^-17), so the scores are those of the fp32 queries up to fp32 accumulation.
 // The value product runs in fp16: the softmax weights are rounded to fp16
 // (2^-11, where bf16 would give 2^-8), and each bf16 latent row is converted
-// to fp16 in registers, exactly for cache values below 65504 in magnitude
-// (bf16 carries 8 significant bits, fp16 11; values under 2^-14 become fp16
-// subnormals, 2^-24 apart).  fp16 weights bound the reference-max headroom:
+// to fp16 in registers: bf16 carries 8 significant bits, fp16 11, so the
+// conversion is exact for magnitudes from 2^-17 (where fp16's subnormal
+// spacing 2^-24 is the bf16 value's last bit) to 65504; smaller values round
+// to that spacing, magnitudes of 65520 or more overflow.  fp16 weights bound the reference-max headroom:
 // a weight exp2(s - m_ref) must stay below 65504, so a tile whose scores pass
 // m_ref by more than kHeadroom triggers the re-sweep.
 //

@@ -22,7 +22,7 @@ TV_Q2_STEP_ASM -- per wave, for tile t (scores) and tile t-1 (values):
      the latent (value) fragments into v[192:223], fragment f at
      v[192 + 4 f], and there converted from bf16 to fp16 in place, CVT_DELAY
      matrix ops after their read (per dword: widen both halves to fp32, then
-     one v_cvt_pk_f16_f32; exact below 65504 in magnitude).
+     one v_cvt_pk_f16_f32; exact for magnitudes from 2^-17 to 65504).
   2. Values O^T[rb][db] (%[o<4 rb + db>], rb = 0, 1: rows 32 rb .. 32 rb + 31)
      += V(db, h) x P(rb, h): 16 x v_mfma_f32_32x32x16_f16, n = 8 h + 2 db + rb.
      V(db, h) (fragment f = 2 h ... as n >> 1) is read from the row-major
@@ -331,8 +331,8 @@ def step_asm() -> str:
 
     def convert_half(f, h):
         """bf16 -> fp16 in place, dwords 2h, 2h + 1 of value fragment f
-        (exact: every bf16 cache value below 65504 in magnitude is an fp16
-        value, subnormal ones rounded to fp16's 2^-24 spacing)."""
+        (exact for magnitudes from 2^-17 to 65504; below that rounded to
+        fp16's 2^-24 spacing)."""
         base = V_BASE + 4 * f
         for d in (base + 2 * h, base + 2 * h + 1):
             emit(f"v_lshlrev_b32 v{CVT_TMP}, 16, v{d}")
