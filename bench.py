@@ -36,11 +36,12 @@ PEAKS_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32_mfma": 157.3, "f32_valu": 15
 # Which kernel the library runs for each cache dtype, the arithmetic it does,
 # and the roofline that bounds it.
 KERNELS = {
+    # (query_terms: the score product runs once per bf16 term of the queries)
     "bf16": dict(name="attn_mfma_q2_kernel",
                  source=["tree_verify_mla_tv_amd/csrc/attn_mfma_q2.hip", "tree_verify_mla_tv_amd/csrc/attn_mfma_q2_asm.h",
                          "tree_verify_mla_tv_amd/csrc/attn_mfma_common.h", "tree_verify_mla_tv_amd/csrc/attn_mfma_asm.h",
                          "tree_verify_mla_tv_amd/csrc/tv_kernels.h"],
-                 bound="mfma", peak="bf16", dtype="bf16"),
+                 bound="mfma", peak="bf16", dtype="bf16", query_terms=2),
     # tv_verify_attn_ex with TV_ATTN_BF16_QUERIES: the queries rounded to one bf16 term
     "bf16_queries": dict(name="attn_mfma_bf16_kernel",
                          source=["tree_verify_mla_tv_amd/csrc/attn_mfma.hip",
@@ -531,6 +532,16 @@ def main() -> int:
                    "timed": "HIP events around 50 back-to-back tv_tree_rope launches (per-launch mean)",
                    "in_step_ms": round(rope_ms, 5),
                    "in_step_timed": "HIP events around each tv_tree_rope call of the timed steps"}
+    if kern.get("query_terms", 1) > 1:
+        # The matrix work the scheme itself does per visible (row, key) pair:
+        # the score product once per query term, the value product once.
+        factor = (kern["query_terms"] * 2 * (w.d_c + w.d_r) + 2 * w.d_c) / (2 * (w.d_c + w.d_r) + 2 * w.d_c)
+        rec["roofline"]["scheme_matrix_work"] = {
+            "what": f"score product over {kern['query_terms']} bf16 query terms: matrix-core flops per algorithmic "
+                    "flop (padding and masked keys not counted)",
+            "factor": round(factor, 4),
+            "tflops": round(achieved_tflops * factor, 1),
+            "frac_of_peak": round(achieved_tflops * factor / peak, 4)}
     if w.kv_dtype == "bf16":
         rec["roofline"]["reference_gemm"] = reference_gemm(torch)
     if args.cpu_sample > 0:
