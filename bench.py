@@ -314,10 +314,25 @@ def fp32_configs(torch, tv, W, with_oracle: bool = False) -> dict:
             fn()
         ms = _time_ms(torch, fn, 200)
         c = algorithmic_counts(w, inp["parent"])
+        mfma = (w.d_c, w.d_r) == (512, 64)
+        # The library's choice of form: 32-row workgroups when the batch has at
+        # most 128 blocks of 64 rows.
+        narrow = mfma and w.B * -(-(w.q_len * w.H) // 64) <= 128
         out[name] = {"us": round(ms * 1e3, 2), "tflops": round(c["flops"] / (ms * 1e-3) / 1e12, 2),
                      "frac_of_fp32_peak": round(c["flops"] / (ms * 1e-3) / 1e12 / PEAKS_TFLOPS["f32_mfma"], 4),
-                     "kernel": "attn_mfma_f32_kernel" if (w.d_c, w.d_r) == (512, 64) else "attn_valu_kernel",
+                     "kernel": ("attn_mfma_f32_narrow_kernel" if narrow else "attn_mfma_f32_kernel") if mfma
+                     else "attn_valu_kernel",
                      "gbs": round(c["attn_bytes"] / (ms * 1e-3) / 1e9, 1)}
+        if narrow:
+            # the 64-row form on the same call, for comparison
+            ws_w = tv.workspace_size(w.B, w.H, w.q_len, w.prefix_len, w.d_c, w.d_r, tv.TV_F32, tv.TV_ATTN_F32_WIDE)
+            wsw = torch.empty(max(ws_w, 1), dtype=torch.uint8, device=dev)
+            fw = lambda: tv.verify_attn_ex(t["q_lat"], t["q_rope"], t["c_kv"], t["k_rope"], t["parent"],
+                                           w.prefix_len, w.sm_scale, tv.TV_ATTN_F32_WIDE, out=o, workspace=wsw)
+            for _ in range(20):
+                fw()
+            ms_w = _time_ms(torch, fw, 200)
+            out[name]["wide_form_us"] = round(ms_w * 1e3, 2)
         if with_oracle:
             cpu_us = cpu_baseline_fp32(w, inp)
             out[name]["cpu_oracle_us"] = round(cpu_us, 1)

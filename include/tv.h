@@ -184,11 +184,18 @@ tv_status_t tv_verify_attn_noalloc(const float* q_lat, const float* q_rope, cons
  *   and no range limit on the latent cache, but every score moves by up to
  *   2^-9 of its terms and every weight by 2^-9; right when the queries are
  *   bf16 values already, or when that error is acceptable).  No effect on
- *   other shapes.  Unknown flag bits return
- *   TV_ERR_INVALID.  The workspace must hold
+ *   other shapes.
+ *   TV_ATTN_F32_WIDE: with an fp32 cache at (512, 64), run every batch on
+ *   the 64-row workgroups.  By default a batch of at most 128 such row
+ *   blocks runs on 32-row workgroups that split each unit's keys in two
+ *   halves (combined by log-sum-exp weights); both forms compute the same
+ *   products in fp32 and agree to fp32 rounding.  For comparisons; no effect
+ *   on other shapes.
+ *   Unknown flag bits return TV_ERR_INVALID.  The workspace must hold
  *   tv_verify_attn_ex_workspace_size(..., flags) bytes.
  */
 #define TV_ATTN_BF16_QUERIES 1u
+#define TV_ATTN_F32_WIDE 2u
 tv_status_t tv_verify_attn_ex(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,
                               const int32_t* parent, int32_t prefix_len, int32_t B, int32_t H, int32_t q_len,
                               int32_t d_c, int32_t d_r, tv_dtype_t kv_dtype, float sm_scale, uint32_t flags,

@@ -265,18 +265,28 @@ def test_verify_attn_noalloc_rejects_before_launch():
 
 def test_verify_attn_ex_flags():
     """tv_verify_attn_ex: flags 0 is tv_verify_attn; TV_ATTN_BF16_QUERIES
-    selects the one-term query kernel (its own workspace size); unknown bits
-    are refused before launch."""
+    selects the one-term query kernel (its own workspace size) and
+    TV_ATTN_F32_WIDE the fp32 kernel's 64-row form (its own workspace size for
+    a small batch); unknown bits are refused before launch."""
     lib = tv.load()
     f = lib.tv_verify_attn_ex
-    assert f(A, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.1, 2, A, None, None, 0, None) == INV     # unknown flag
+    assert (tv.TV_ATTN_BF16_QUERIES, tv.TV_ATTN_F32_WIDE) == (1, 2)
+    assert f(A, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.1, 4, A, None, None, 0, None) == INV     # unknown flag
     assert f(A, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.1, 1 << 31, A, None, None, 0, None) == INV
     assert f(None, A, A, A, A, 4, 1, 2, 3, 64, 32, 0, 0.1, 1, A, None, None, 0, None) == INV
     assert f(A, A, A, A, A, 4, 1, 2, 257, 64, 32, 0, 0.1, 1, A, None, None, 0, None) == UNS
     ws = lib.tv_verify_attn_ex_workspace_size
-    assert ws(32, 64, 33, 8192, 512, 64, 1, 2) == 0                   # unknown flag
+    assert ws(32, 64, 33, 8192, 512, 64, 1, 4) == 0                   # unknown flag
     # serving batch: 64-row blocks with two-term queries, 128-row blocks with one
     two, one = ws(32, 64, 33, 8192, 512, 64, 1, 0), ws(32, 64, 33, 8192, 512, 64, 1, 1)
     assert two == tv.workspace_size(32, 64, 33, 8192, 512, 64, tv.TV_BF16) and 0 < two < one
-    # the flag changes nothing for the fp32 cache
+    # the bf16-queries flag changes nothing for the fp32 cache, the wide flag
+    # nothing for the bf16 cache
     assert ws(2, 64, 9, 5000, 512, 64, 0, 1) == ws(2, 64, 9, 5000, 512, 64, 0, 0)
+    assert ws(32, 64, 33, 8192, 512, 64, 1, 2) == two and ws(32, 64, 33, 8192, 512, 64, 1, 3) == one
+    # a small fp32 batch: 32-row blocks by default (two splits' partials per
+    # 64 rows of the wide form's one), the wide form on request
+    narrow, wide = ws(2, 64, 9, 5000, 512, 64, 0, 0), ws(2, 64, 9, 5000, 512, 64, 0, 2)
+    assert narrow > 0 and wide > 0 and narrow != wide
+    # a batch of more than 128 64-row blocks takes the wide form either way
+    assert ws(3, 64, 44, 5000, 512, 64, 0, 0) == ws(3, 64, 44, 5000, 512, 64, 0, 2)

@@ -150,6 +150,8 @@ EDGE = [
     (5, 3, 17, 64, 512, 64, "f32", "wide"),       # prefix of exactly two tiles, partial row block
     (2, 64, 33, 700, 512, 64, "f32", "branch4"),  # full 64-row blocks, kv pieces
     (4, 16, 8, 0, 512, 64, "f32", "chain"),       # R = 128: two full blocks, causal prefill
+    (3, 64, 44, 40, 512, 64, "f32", "rrt"),       # 132 blocks of 64 rows: the 64-row form by default
+    (9, 64, 30, 20, 512, 64, "f32", "branch4"),   # 270 such blocks: the last blocks cut into kv pieces
 ]
 
 
@@ -322,8 +324,17 @@ def test_bf16_late_large_scores_resweep(rise):
               "bf16_queries")
 
 
-# The three attention kernels: (d_c, d_r, cache dtype) that selects each.
-KERNELS = {"mfma_bf16": (512, 64, "bf16"), "mfma_f32": (512, 64, "f32"), "valu": (64, 32, "f32")}
+# The attention kernels: (d_c, d_r, cache dtype) that selects each, and the
+# tv_verify_attn_ex flags.  The fp32 matrix-core kernel takes these tests'
+# small batches on its 32-row form by default; TV_ATTN_F32_WIDE keeps them on
+# the 64-row form.
+KERNELS = {"mfma_bf16": (512, 64, "bf16"), "mfma_f32": (512, 64, "f32"), "mfma_f32_wide": (512, 64, "f32"),
+           "valu": (64, 32, "f32")}
+KERNEL_FLAGS = {"mfma_f32_wide": tv.TV_ATTN_F32_WIDE}
+
+
+def _attn(kernel, *args, **kw):
+    return tv.verify_attn_ex(*args, flags=KERNEL_FLAGS.get(kernel, 0), **kw)
 
 
 def _check_tol(e, dt, tag):
@@ -340,7 +351,8 @@ def test_tree_key_at_every_tile_position(kernel, q):
     pieces (B = 1 splits the kv range, B = 256 does not), on each kernel.
     The fp32 matrix-core kernel once dropped a visible tree key held in score
     register 0 of a later tile; every case here is checked against the
-    oracle."""
+    oracle.  (Its 32-row form takes B = 1 by default, B = 256 takes the
+    64-row form either way.)"""
     d_c, d_r, dt = KERNELS[kernel]
     for B, H in ((1, 16), (256, 4)):
         rng = np.random.default_rng(B + q)
@@ -357,8 +369,8 @@ def test_tree_key_at_every_tile_position(kernel, q):
         for P in range(28, 72):
             ck = np.ascontiguousarray(ck_all[:, :P + q])
             kr = np.ascontiguousarray(kr_all[:, :P + q])
-            out = tv.verify_attn(*args, cuda_cache(ck, dt), cuda_cache(kr, dt), torch.from_numpy(par).cuda(), P,
-                                 0.04).cpu().numpy()
+            out = _attn(kernel, *args, cuda_cache(ck, dt), cuda_cache(kr, dt), torch.from_numpy(par).cuda(), P,
+                        0.04).cpu().numpy()
             ref, _ = O.verify_attn(ql[rows].astype(np.float64), qr[rows].astype(np.float64),
                                    O.as_f64(ck[rows], dt), O.as_f64(kr[rows], dt), par[rows], P, 0.04)
             _check_tol(errors(out[rows], ref), dt, (kernel, B, P, q))
@@ -385,8 +397,8 @@ def test_zero_queries_give_visible_mean(kernel, P):
     _, _, c_kv, k_rope, parent = _edge_inputs(B, H, q, P, d_c, d_r, dt, "branch4", seed=40 + P)
     z_lat = np.zeros((B, q, H, d_c), np.float32)
     z_rope = np.zeros((B, q, H, d_r), np.float32)
-    out, lse = tv.verify_attn(cuda_f32(z_lat), cuda_f32(z_rope), cuda_cache(c_kv, dt), cuda_cache(k_rope, dt),
-                              torch.from_numpy(parent).cuda(), P, 0.04, return_lse=True)
+    out, lse = _attn(kernel, cuda_f32(z_lat), cuda_f32(z_rope), cuda_cache(c_kv, dt), cuda_cache(k_rope, dt),
+                     torch.from_numpy(parent).cuda(), P, 0.04, return_lse=True)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
     C = O.as_f64(c_kv, dt)
@@ -451,8 +463,8 @@ def test_topological_relabelling_permutes_outputs(kernel):
         qr2[b, new] = q_rope[b]
         ck2[b, P + new] = c_kv[b, P:]
         kr2[b, P + new] = k_rope[b, P:]
-    run = lambda a, bq, c, k, p: tv.verify_attn(cuda_f32(a), cuda_f32(bq), cuda_cache(c, dt), cuda_cache(k, dt),
-                                                torch.from_numpy(p).cuda(), P, 0.04).cpu().numpy()
+    run = lambda a, bq, c, k, p: _attn(kernel, cuda_f32(a), cuda_f32(bq), cuda_cache(c, dt), cuda_cache(k, dt),
+                                       torch.from_numpy(p).cuda(), P, 0.04).cpu().numpy()
     o1, o2 = run(q_lat, q_rope, c_kv, k_rope, parent), run(ql2, qr2, ck2, kr2, par2)
     back = np.stack([o2[b, news[b]] for b in range(B)])
     e = errors(back, o1)
@@ -460,6 +472,33 @@ def test_topological_relabelling_permutes_outputs(kernel):
     ref, _ = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, dt),
                            O.as_f64(k_rope, dt), parent, P, 0.04)
     _check_tol(errors(o1, ref), dt, kernel)
+
+
+# ---------------------------------------------------------------------------
+# The fp32 kernel's 64-row form on the small shapes (TV_ATTN_F32_WIDE)
+# ---------------------------------------------------------------------------
+F32_EDGE = [c for c in EDGE if c[4:7] == (512, 64, "f32")]
+
+
+@pytest.mark.parametrize("case", F32_EDGE, ids=[f"B{c[0]}H{c[1]}q{c[2]}P{c[3]}{c[7]}" for c in F32_EDGE])
+def test_f32_wide_edge_shapes(case):
+    """The fp32-cache edge shapes on the 64-row form, against the oracle and
+    against the default (32-row) form: the same fp32 products, summed in
+    another order where a unit's keys are cut differently."""
+    B, H, q, P, d_c, d_r, dt, kind = case
+    q_lat, q_rope, c_kv, k_rope, parent = _edge_inputs(B, H, q, P, d_c, d_r, dt, kind, seed=B * 1000 + q)
+    sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
+    ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, dt),
+                                     O.as_f64(k_rope, dt), parent, P, sm)
+    args = (cuda_f32(q_lat), cuda_f32(q_rope), cuda_cache(c_kv, dt), cuda_cache(k_rope, dt),
+            torch.from_numpy(parent).cuda(), P, sm)
+    out, lse = tv.verify_attn_ex(*args, tv.TV_ATTN_F32_WIDE, return_lse=True)
+    out0, lse0 = tv.verify_attn(*args, return_lse=True)
+    out, lse, out0, lse0 = (t.cpu().numpy() for t in (out, lse, out0, lse0))
+    check_out("edge-wide", str(case), torch.from_numpy(out), torch.from_numpy(lse), ref_out, ref_lse, dt)
+    e = errors(out, out0)
+    assert e["max_abs"] <= 1e-5 and e["max_rel"] <= 1e-2, (case, e)
+    assert np.abs(lse - lse0).max() <= 4e-5, case
 
 
 # ---------------------------------------------------------------------------

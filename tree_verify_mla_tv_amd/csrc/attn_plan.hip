@@ -79,8 +79,18 @@ AttnPlan plan_attention(const AttnShape& s) {
   AttnPlan p{};
   choose_kernel(s, p);
   const bool mfma = p.kernel == AttnKernel::kMfmaBf16 || p.kernel == AttnKernel::kMfmaBf16Q2;
-  const bool f32 = p.kernel == AttnKernel::kMfmaF32;
   const int R = s.q_len * s.H;
+  if (p.kernel == AttnKernel::kMfmaF32 && !s.f32_wide &&
+      static_cast<long long>(s.B) * ceil_div(R, kF32Rows) <= kNumCU / 2) {
+    // At most half a round of 64-row blocks: the narrow form (32-row blocks,
+    // each unit's keys in two halves) gives every kv piece twice the
+    // workgroups, pads fewer rows, and its pieces' partial results are half
+    // the wide form's for the same work per workgroup.  With more blocks the
+    // wide form reads each key tile for twice the rows.
+    p.kernel = AttnKernel::kMfmaF32Narrow;
+    p.rows_per_block = kF32NarrowRows;
+  }
+  const bool f32 = p.kernel == AttnKernel::kMfmaF32 || p.kernel == AttnKernel::kMfmaF32Narrow;
   p.n_rb = ceil_div(R, p.rows_per_block);
   bool has_tail = (R % p.rows_per_block) != 0;
   // Workgroups resident per CU: a matrix-core kernel takes a whole CU; the VALU
@@ -182,7 +192,8 @@ AttnPlan plan_attention_ragged(const AttnShape& s) {
 
 namespace {
 
-static_assert(kMfmaKeys == kPlanTile && kValuKeys == kPlanTile && kF32Keys == kPlanTile,
+static_assert(kMfmaKeys == kPlanTile && kValuKeys == kPlanTile && kF32Keys == kPlanTile &&
+                  2 * kF32NarrowKeys == kPlanTile,
               "plans count tiles of 32 keys for every kernel");
 
 // Lengths of request b as the prep kernel clamped them (into the bounds and
@@ -662,7 +673,8 @@ hipError_t launch_attention(const AttnShape& s, const AttnPlan& plan, const Attn
   if (a.req) lp.units = plan.units < plan.target ? plan.units : plan.target;
   hipError_t e = lp.kernel == AttnKernel::kMfmaBf16Q2 ? launch_attn_mfma_q2(s, lp, a, stream)
                  : lp.kernel == AttnKernel::kMfmaBf16 ? launch_attn_mfma_bf16(s, lp, a, stream)
-                 : lp.kernel == AttnKernel::kMfmaF32  ? launch_attn_mfma_f32(s, lp, a, stream)
+                 : lp.kernel == AttnKernel::kMfmaF32 || lp.kernel == AttnKernel::kMfmaF32Narrow
+                     ? launch_attn_mfma_f32(s, lp, a, stream)
                                                       : launch_attn_valu(s, lp, a, stream);
   if (e != hipSuccess || plan.merge_blocks == 0) return e;
   if (a.req) {

@@ -39,7 +39,7 @@ void* scratch_on_current_device() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Flags tv_verify_attn_ex knows.
-constexpr uint32_t kAttnFlags = TV_ATTN_BF16_QUERIES;
+constexpr uint32_t kAttnFlags = TV_ATTN_BF16_QUERIES | TV_ATTN_F32_WIDE;
 
 // Most rotated pairs one RoPE launch takes (its grid strides over them).
 constexpr int64_t kMaxRopePairs = int64_t{1} << 40;
@@ -77,7 +77,8 @@ tv_status_t check_attn_shape(int32_t prefix_len, int32_t B, int32_t H, int32_t q
 tv::AttnShape make_shape(int32_t prefix_len, int32_t B, int32_t H, int32_t q_len, int32_t d_c, int32_t d_r,
                          tv_dtype_t kv_dtype, uint32_t flags = 0) {
   return tv::AttnShape{B,   H,   q_len, prefix_len, prefix_len + q_len,
-                       d_c, d_r, kv_dtype == TV_BF16, (flags & TV_ATTN_BF16_QUERIES) != 0};
+                       d_c, d_r, kv_dtype == TV_BF16, (flags & TV_ATTN_BF16_QUERIES) != 0,
+                       (flags & TV_ATTN_F32_WIDE) != 0};
 }
 
 tv_status_t run_attention(const float* q_lat, const float* q_rope, const void* c_kv, const void* k_rope,

@@ -35,7 +35,7 @@ hipError_t launch_tree_rope_ragged(float* q_rope, void* k_rope, bool bf16, const
 // ---------------------------------------------------------------------------
 // Attention
 // ---------------------------------------------------------------------------
-enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1, kMfmaF32 = 2, kMfmaBf16Q2 = 3 };
+enum class AttnKernel : int { kValu = 0, kMfmaBf16 = 1, kMfmaF32 = 2, kMfmaBf16Q2 = 3, kMfmaF32Narrow = 4 };
 
 // Workgroup geometry of the kernels: the bf16-cache matrix-core kernels (d_c
 // 512, d_r 64; queries as two bf16 terms by default, or rounded to one on
@@ -51,6 +51,11 @@ constexpr int kMfmaThreads = 256;
 constexpr int kF32Rows = 64;      // 4 waves x 16 query rows
 constexpr int kF32Keys = 32;
 constexpr int kF32Threads = 256;
+// The fp32 kernel's narrow form (uniform batches with few 64-row blocks): 32
+// query rows, the unit's keys cut in two halves of 16-key tiles, one pair of
+// waves per half.  Its plans count tiles of 32 keys, one 16-key tile per half.
+constexpr int kF32NarrowRows = 32;
+constexpr int kF32NarrowKeys = 16;
 // Tiles of a unit that hold tree keys or the unit's range end: at most
 // q_len / 32 + 2.
 constexpr int kMaxBoundaryTiles = kMaxQ / kMfmaKeys + 2;
@@ -87,6 +92,7 @@ struct AttnShape {
   int B, H, q_len, prefix_len, kv_len, d_c, d_r;
   bool kv_bf16;
   bool bf16_queries;  // bf16 cache at (512, 64): round the scaled queries to one bf16 term
+  bool f32_wide;      // fp32 cache at (512, 64): the 64-row form at every size (no narrow form)
 };
 
 AttnPlan plan_attention(const AttnShape& s);

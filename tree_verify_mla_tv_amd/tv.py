@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libtv.so")
 
 TV_OK, TV_ERR_INVALID, TV_ERR_UNSUPPORTED, TV_ERR_LAUNCH = 0, 1, 2, 3
 TV_ATTN_BF16_QUERIES = 1
+TV_ATTN_F32_WIDE = 2
 TV_F32, TV_BF16 = 0, 1
 TV_MAX_Q_LEN = 256
 TV_MAX_BUILD_BUDGET = TV_MAX_Q_LEN - 1
@@ -237,7 +238,8 @@ def verify_attn_ex(q_lat, q_rope, c_kv, k_rope, parent, prefix_len: int, sm_scal
                    flags: int = 0, out=None, lse=None, return_lse: bool = False, workspace=None):
     """verify_attn with option flags (tv_verify_attn_ex; flags 0 calls
     tv_verify_attn).  TV_ATTN_BF16_QUERIES rounds the scaled queries to one
-    bf16 term on the bf16-cache matrix-core path."""
+    bf16 term on the bf16-cache matrix-core path; TV_ATTN_F32_WIDE keeps an
+    fp32-cache batch at (512, 64) on the 64-row workgroups at every size."""
     B, q, H, d_c, d_r = _attn_shapes(q_lat, q_rope, c_kv, k_rope, parent, prefix_len)
     dt = _kv_dtype(c_kv)
     if sm_scale is None:
