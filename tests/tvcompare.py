@@ -78,7 +78,10 @@ def rope_mismatch(got, ref, x_raw, dtype: str, max_pos: int):
 
 
 def lse_bound(kind, ref_lse):
-    """Allowed |lse - ref| per row.  f32: scores rounded at ~1e-7 relative.
+    """Allowed |lse - ref| per row.  f32: scores rounded at ~1e-7 relative,
+    and the lse is itself an fp32 number (taken in base 2, then scaled by
+    ln 2): 2e-5 plus 2^-20 of |lse| (eight fp32 ulps of a value that size; at
+    |lse| ~ 100 a few ulps of the max score alone exceed 2e-5).
     bf16 (the default bf16-cache kernel): scores to fp32 precision, softmax
     weights rounded to fp16 (each within 2^-11 relative, so the log of their
     sum moves by at most ~2^-11): 2^-10 plus 2^-14 of |lse|.  bf16_queries (the
@@ -86,7 +89,7 @@ def lse_bound(kind, ref_lse):
     few 2^-9 of its terms: 2^-8 plus 2^-12 of |lse|."""
     r = np.abs(np.asarray(ref_lse, np.float64))
     if kind == "f32":
-        return np.full_like(r, 2e-5)
+        return 2e-5 + 2.0 ** -20 * r
     if kind == "bf16":
         return 2.0 ** -10 + 2.0 ** -14 * r
     if kind == "bf16_queries":
