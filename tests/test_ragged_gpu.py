@@ -167,7 +167,8 @@ def test_ragged_many_row_blocks_tail_pieces():
     _check(q_lens, prefixes, 64, 512, 64, "bf16")
 
 
-@pytest.mark.parametrize("which", ["bench_like", "uniform", "few_long", "many_short", "valu", "f32_mfma"])
+@pytest.mark.parametrize("which", ["bench_like", "uniform", "few_long", "many_short", "valu", "f32_mfma",
+                                   "f32_mfma_wide"])
 def test_ragged_records_match_plan_model(which):
     """The prep kernel's records (plan choice, class order, numbering) equal
     the host model's word for word, and the attention over them matches the
@@ -189,10 +190,14 @@ def test_ragged_records_match_plan_model(which):
         dt, H, d_c, d_r = "f32", 4, 128, 32
         q_lens = [int(x) for x in rng.integers(1, 70, 12)]
         prefixes = [int(x) for x in rng.integers(0, 9000, 12)]
-    else:
+    elif which == "f32_mfma":  # the fp32 kernel's 32-row form (10 x 9 blocks of 64 rows at most)
         dt, H, d_c, d_r = "f32", 8, 512, 64
         q_lens = [int(x) for x in rng.integers(1, 70, 10)]
         prefixes = [int(x) for x in rng.integers(0, 5000, 10)]
+    else:  # its 64-row form (6 x 33 blocks of 64 rows at most)
+        dt, H, d_c, d_r = "f32", 64, 512, 64
+        q_lens = [int(x) for x in rng.integers(9, 34, 6)]
+        prefixes = [int(x) for x in rng.integers(0, 1500, 6)]
     max_q = max(q_lens)
     print(f"ragged records {which} B={len(q_lens)}", flush=True)
     q_lat, q_rope, c_kv, k_rope, parent = _ragged_inputs(q_lens, prefixes, H, d_c, d_r, dt, 5, seed=1)
@@ -207,7 +212,12 @@ def test_ragged_records_match_plan_model(which):
                                 torch.tensor(q_lens, dtype=torch.int32).cuda(), max_q, sm, workspace=ws)
     torch.cuda.synchronize()
     if d_c == 512 and d_r == 64:  # the matrix-core kernels: rows per workgroup, workgroups at once, costs
-        rpb, target, cost = (64, 256, RP.COST_DEFAULT) if dt == "bf16" else (64, 256, RP.COST_F32)
+        if dt == "bf16":
+            rpb, target, cost = 64, 256, RP.COST_DEFAULT
+        else:  # the 32-row form when the bound has at most 128 blocks of 64 rows
+            narrow = len(q_lens) * -(-(max_q * H) // 64) <= 128
+            assert narrow == (which == "f32_mfma")
+            rpb, target, cost = (32 if narrow else 64), 256, RP.COST_F32
     else:
         rpb, target, cost = 16, 512, RP.COST_DEFAULT
     model = RP.records_words(RP.plan(prefixes, q_lens, H, max_q, S, rpb, target, cost))

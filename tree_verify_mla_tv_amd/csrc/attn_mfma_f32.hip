@@ -686,16 +686,22 @@ __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_ragged_kernel(At
   for_each_ragged_unit([](const AttnArgs& a, const Unit& w) { attn_mfma_f32_unit(a, w); });
 }
 
-// The narrow form, uniform batches only.
+// The narrow form: a uniform batch, one unit per workgroup; a ragged batch, a
+// persistent grid.
 __global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_narrow_kernel(AttnArgs a) {
   attn_mfma_f32_narrow_unit(a, decode_unit(a, unit_of_block(a, blockIdx.x)));
+}
+__global__ __launch_bounds__(kF32Threads, 1) void attn_mfma_f32_narrow_ragged_kernel(AttnArgs) {
+  for_each_ragged_unit([](const AttnArgs& a, const Unit& w) { attn_mfma_f32_narrow_unit(a, w); });
 }
 
 hipError_t launch_attn_mfma_f32(const AttnShape& s, const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(plan.units));
   if (plan.kernel == AttnKernel::kMfmaF32Narrow) {
-    if (a.req) return hipErrorNotSupported;
-    attn_mfma_f32_narrow_kernel<<<grid, kF32Threads, 0, stream>>>(a);
+    if (a.req)
+      attn_mfma_f32_narrow_ragged_kernel<<<grid, kF32Threads, 0, stream>>>(a);
+    else
+      attn_mfma_f32_narrow_kernel<<<grid, kF32Threads, 0, stream>>>(a);
   } else if (a.req)
     attn_mfma_f32_ragged_kernel<<<grid, kF32Threads, 0, stream>>>(a);
   else

@@ -180,7 +180,9 @@ struct PlanCost {
   int pieces_per_step;  // split pieces the merge pass combines per tile-step of the whole GPU
 };
 // The bf16 matrix-core and the VALU kernels: a unit's set-up is ~10 of their
-// tile-steps; the fp32 matrix-core kernel's tile-step is ~5x longer.
+// tile-steps; the fp32 matrix-core kernel's (its 32-row form: one 16-key tile
+// per half per 32-key plan tile) is several times longer, and its set-up
+// about one.
 constexpr PlanCost kPlanCostDefault{10, 8, 16};
 constexpr PlanCost kPlanCostF32{1, 1, 80};
 constexpr int kPlanBody = 4, kPlanTail = 5;
