@@ -55,12 +55,40 @@ KERNELS = {
 }
 
 
+def strip_comments(text: str) -> str:
+    """C/C++ source without its // and /* */ comments (string and character
+    literals kept whole), whitespace runs collapsed: edits to comments or
+    layout leave it unchanged, any change to the code does not."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(rels) -> str:
-    """First 16 hex digits of sha256 over the kernel's source files, in order."""
+    """First 16 hex digits of sha256 over the kernel's source files, in order,
+    each without its comments (strip_comments)."""
     h = hashlib.sha256()
     for rel in rels:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 
