@@ -509,6 +509,26 @@ def test_f32_late_large_scores_resweep(rise, wide):
               ref_out, ref_lse, "f32")
 
 
+def test_f32_row_block_and_piece_edges():
+    """fp32 cache at 512/64, both forms: row counts on either side of the
+    32- and 64-row blocks (R = 31 .. 97 with one head) over prefixes that
+    give the 32-row form's units an odd or even number of 16-key tiles, one
+    tile, or a half with no keys, each against the oracle."""
+    sm = float(np.float32(1.0 / np.sqrt(576.0)))
+    for q in (31, 32, 33, 63, 64, 65, 95, 97):
+        for P in (0, 5, 300, 1000):
+            B, H = 2, 1
+            seed = 7000 + 10 * q + P
+            q_lat, q_rope, c_kv, k_rope, parent = _edge_inputs(B, H, q, P, 512, 64, "f32", "rrt", seed=seed)
+            ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat, "f32"), O.as_f64(q_rope, "f32"), O.as_f64(c_kv, "f32"),
+                                             O.as_f64(k_rope, "f32"), parent, P, sm)
+            args = (cuda_f32(q_lat), cuda_f32(q_rope), cuda_f32(c_kv), cuda_f32(k_rope),
+                    torch.from_numpy(parent).cuda(), P, sm)
+            for flags in (0, tv.TV_ATTN_F32_WIDE):
+                out, lse = tv.verify_attn_ex(*args, flags, return_lse=True)
+                check_out(f"f32 edges flags={flags}", f"B{B} H{H} q{q} P{P}", out, lse, ref_out, ref_lse, "f32")
+
+
 # ---------------------------------------------------------------------------
 # The fp32 kernel's 64-row form on the small shapes (TV_ATTN_F32_WIDE)
 # ---------------------------------------------------------------------------
