@@ -221,7 +221,18 @@ __device__ __forceinline__ ReqLen req_len(const int32_t* rq, int b, int H, int r
   return r;
 }
 
+// The same from the clamped lengths (q, P) of the request.
+__device__ __forceinline__ ReqLen req_len_of(int q, int P, int H, int rpb) {
+  ReqLen r;
+  r.q = q;
+  r.P = P;
+  r.nblk = (q * H + rpb - 1) / rpb;
+  r.tiles = (P + q + kPlanTile - 1) / kPlanTile;
+  return r;
+}
+
 constexpr int kPrepThreads = 1024;
+constexpr int kPrepLdsReqs = 2048;  // requests whose clamped lengths the prep kernel keeps in LDS
 constexpr int kSortMax = 4096;  // classes sorted in LDS (B <= 2048); larger batches keep request order
 constexpr int kRankSortMax = 256;  // up to this many classes by rank (two barriers), more by a bitonic network
 
@@ -283,7 +294,14 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   __shared__ int s_choice;
   __shared__ int s_scan[kPrepThreads / 64];
   __shared__ unsigned long long s_sort[kSortMax];
+  __shared__ int s_len[kPrepLdsReqs][2];  // clamped (q_len, prefix) per request, for B <= kPrepLdsReqs
   const int t = threadIdx.x;
+  // Every phase after the first reads the clamped lengths: from LDS when the
+  // batch fits (one global round trip fewer per phase), else from the records.
+  const bool in_lds = B <= kPrepLdsReqs;
+  auto lengths = [&](int b) {
+    return in_lds ? req_len_of(s_len[b][0], s_len[b][1], H, rpb) : req_len(rq, b, H, rpb);
+  };
   const int per = (B + kPrepThreads - 1) / kPrepThreads;
   const int b0 = min(B, t * per), b1 = min(B, b0 + per);
 
@@ -300,15 +318,20 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
       const int q = min(max(q_len[b], 0), max_q);
       const int qc = min(q, max(0, n_nodes - o_raw));
       o_raw += q;
+      const int pc = min(max(prefix_len[b], 0), kv_stride - qc);
       rq[b * kReqFields + kReqQLen] = qc;
-      rq[b * kReqFields + kReqPrefix] = min(max(prefix_len[b], 0), kv_stride - qc);
+      rq[b * kReqFields + kReqPrefix] = pc;
+      if (in_lds) {
+        s_len[b][0] = qc;
+        s_len[b][1] = pc;
+      }
     }
     __syncthreads();
   }
 
   long long w0 = 0, wt = 0;
   for (int b = b0; b < b1; ++b) {
-    const ReqLen r = req_len(rq, b, H, rpb);
+    const ReqLen r = lengths(b);
     w0 += static_cast<long long>(r.nblk) * (r.tiles + cost.setup);
     wt += static_cast<long long>(r.nblk) * r.tiles;
   }
@@ -326,7 +349,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   // One (request, candidate) pair per thread at a time.
   for (int i = t; i < B * kPlanCands; i += kPrepThreads) {
     const int b = i / kPlanCands, c = i - b * kPlanCands;
-    const ReqLen r = req_len(rq, b, H, rpb);
+    const ReqLen r = lengths(b);
     if (r.nblk == 0) continue;
     const ReqCut k = cut_request(r.tiles, s_capb[c], s_capt[c]);
     const int last_b = r.tiles - (k.n_body - 1) * k.c_body, last_t = r.tiles - (k.n_tail - 1) * k.c_tail;
@@ -394,7 +417,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   // Per request: nodes, slots, merged blocks (request order).
   int n_q = 0, n_slot = 0, n_merge = 0;
   for (int b = b0; b < b1; ++b) {
-    const ReqLen r = req_len(rq, b, H, rpb);
+    const ReqLen r = lengths(b);
     if (r.nblk == 0) continue;
     const ReqCut k = cut_request(r.tiles, cap_b, cap_t);
     n_q += r.q;
@@ -406,7 +429,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   int o_slot = block_scan(n_slot, s_scan, &tot_slot);
   int o_merge = block_scan(n_merge, s_scan, &tot_merge);
   for (int b = b0; b < b1; ++b) {
-    const ReqLen r = req_len(rq, b, H, rpb);
+    const ReqLen r = lengths(b);
     ReqCut k{1, r.tiles, 1, r.tiles};
     if (r.nblk > 0) k = cut_request(r.tiles, cap_b, cap_t);
     int32_t* o = rq + b * kReqFields;
@@ -440,7 +463,7 @@ __global__ __launch_bounds__(kPrepThreads) void ragged_prep_kernel(const int32_t
   const int n_cls = 2 * B;
   const bool sorted = n_cls <= kSortMax;
   auto cls_of = [&](int id, int& units, int& len) {
-    const ReqLen r = req_len(rq, id >> 1, H, rpb);
+    const ReqLen r = lengths(id >> 1);
     units = 0;
     len = 0;
     if (r.nblk == 0) return;
