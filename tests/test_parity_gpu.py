@@ -144,6 +144,8 @@ EDGE = [
     (1, 3, 64, 1, 512, 64, "bf16", "rrt"),        # largest tree, 1-row prefix
     (2, 64, 9, 4097, 512, 64, "bf16", "branch4"), # few blocks: every block split
     (5, 32, 17, 333, 512, 64, "bf16", "wide"),    # ragged rows and kv tail
+    (1, 128, 33, 100, 512, 64, "bf16", "branch4"),  # 128 heads
+    (2, 7, 19, 333, 512, 64, "bf16", "rrt"),       # odd head count: nodes straddle row blocks
     # fp32 cache, d_c = 512, d_r = 64: the fp32 matrix-core kernel
     (3, 1, 256, 0, 512, 64, "f32", "rrt"),        # tree keys only, 4-word masks, 4 row blocks
     (1, 1, 1, 0, 512, 64, "f32", "chain"),        # one row, one key
@@ -152,6 +154,8 @@ EDGE = [
     (4, 16, 8, 0, 512, 64, "f32", "chain"),       # R = 128: two full blocks, causal prefill
     (3, 64, 44, 40, 512, 64, "f32", "rrt"),       # 132 blocks of 64 rows: the 64-row form by default
     (9, 64, 30, 20, 512, 64, "f32", "branch4"),   # 270 such blocks: the last blocks cut into kv pieces
+    (1, 256, 9, 64, 512, 64, "f32", "chain"),     # 256 heads
+    (2, 7, 19, 333, 512, 64, "f32", "rrt"),       # odd head count: nodes straddle row blocks
 ]
 
 
