@@ -77,6 +77,8 @@ CASES = [
     ([33, 33], [100000, 100], 16, 512, 64, "bf16"),                   # one long request: its own kv pieces
     ([1, 7, 65, 200], [0, 40, 129, 5], 3, 64, 32, "f32"),             # VALU kernel, multi-word trees
     ([130, 2, 256], [7000, 1, 300], 2, 512, 64, "f32"),
+    ([0, 9, 0, 33], [50, 200, 0, 1000], 16, 512, 64, "f32"),         # empty requests, the fp32 32-row form
+    ([33] * 6, [900, 40, 2500, 0, 64, 1500], 64, 512, 64, "f32"),    # the fp32 64-row form (6 x 33 blocks)
     ([3, 1], [0, 0], 1, 128, 64, "bf16"),                              # no prefix at all
 ]
 
