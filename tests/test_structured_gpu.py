@@ -71,6 +71,11 @@ def test_outlier_channels_heavy_tails_f32():
     _run(*_outlier_inputs(), "f32", "outliers f32")
 
 
+def test_outlier_channels_heavy_tails_f32_wide():
+    """The same on the fp32 kernel's 64-row form (TV_ATTN_F32_WIDE)."""
+    _run(*_outlier_inputs(), "f32", "outliers f32 64-row", flags=tv.TV_ATTN_F32_WIDE)
+
+
 def test_outlier_channels_heavy_tails_bf16():
     """The bf16-cache kernel carries each scaled query as two bf16 terms, so
     the dominant score terms keep fp32 precision: within the bf16 bound of
@@ -87,7 +92,12 @@ def test_outlier_channels_heavy_tails_bf16_queries():
     _run(*_outlier_inputs(), "bf16", "outliers bf16 queries", flags=tv.TV_ATTN_BF16_QUERIES)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32", "bf16_queries"])
+# cache dtype and tv_verify_attn_ex flags of each variant
+VARIANTS = {"bf16": ("bf16", 0), "f32": ("f32", 0), "f32_wide": ("f32", tv.TV_ATTN_F32_WIDE),
+            "bf16_queries": ("bf16", tv.TV_ATTN_BF16_QUERIES)}
+
+
+@pytest.mark.parametrize("dt", list(VARIANTS))
 def test_nearly_one_hot(dt):
     """Each query row equals one visible key row scaled up: its softmax puts
     almost all the weight on that key (scores up to ~60 apart in log2)."""
@@ -100,16 +110,14 @@ def test_nearly_one_hot(dt):
                 q_lat[b, i, h] = c_kv[b, j] * 0.5
                 q_rope[b, i, h] = k_rope[b, j] * 0.5
     sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
-    _run(q_lat, q_rope, c_kv, k_rope, parent, P, sm, dt[:4] if dt != "f32" else dt, f"one-hot {dt}",
-         flags=tv.TV_ATTN_BF16_QUERIES if dt == "bf16_queries" else 0)
+    _run(q_lat, q_rope, c_kv, k_rope, parent, P, sm, VARIANTS[dt][0], f"one-hot {dt}", flags=VARIANTS[dt][1])
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32", "bf16_queries"])
+@pytest.mark.parametrize("dt", list(VARIANTS))
 def test_nearly_uniform(dt):
     """A tiny softmax scale: every visible key weighs about the same, so the
     output is close to the mean of the visible latent rows (long sums of
     nearly equal weights)."""
     B, H, q, P, d_c, d_r = 2, 8, 33, 5000, 512, 64
     rng, q_lat, q_rope, c_kv, k_rope, parent = _base(B, H, q, P, d_c, d_r, 3)
-    _run(q_lat, q_rope, c_kv, k_rope, parent, P, 1e-4, dt[:4] if dt != "f32" else dt, f"uniform {dt}",
-         flags=tv.TV_ATTN_BF16_QUERIES if dt == "bf16_queries" else 0)
+    _run(q_lat, q_rope, c_kv, k_rope, parent, P, 1e-4, VARIANTS[dt][0], f"uniform {dt}", flags=VARIANTS[dt][1])
