@@ -41,7 +41,7 @@ def _cache(a, dt):
 
 
 CASES = [
-    # B, H, q, P, dtype, heads checked
+    # B, H, q, P, dtype, heads checked[, tv_verify_attn_ex flags]
     (1, 64, 33, 8192, "bf16", (0, 21, 63)),
     (1, 64, 33, 32768, "bf16", (0, 21, 63)),
     (1, 64, 33, 131072, "bf16", (0, 63)),
@@ -52,18 +52,21 @@ CASES = [
     (1, 8, 33, 32768, "f32", (0, 7)),
     (1, 8, 33, 131072, "f32", (0, 7)),
     (1, 8, 33, 200000, "f32", (0, 7)),
+    (1, 8, 33, 200000, "f32", (0, 7), tv.TV_ATTN_F32_WIDE),  # the fp32 kernel's 64-row form
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}q{c[2]}P{c[3]}{c[4]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}q{c[2]}P{c[3]}{c[4]}" + ("wide" if len(c) > 6 else "")
+                                             for c in CASES])
 def test_long_prefix(case):
-    B, H, q, P, dt, heads = case
+    B, H, q, P, dt, heads = case[:6]
+    flags = case[6] if len(case) > 6 else 0
     d_c, d_r = 512, 64
     print(f"long prefix case {case}", flush=True)
     q_lat, q_rope, c_kv, k_rope, parent = _inputs(B, H, q, P, d_c, d_r, dt, seed=P + H + B)
     sm = float(np.float32(1.0 / np.sqrt(d_c + d_r)))
-    out, lse = tv.verify_attn(torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(), _cache(c_kv, dt),
-                              _cache(k_rope, dt), torch.from_numpy(parent).cuda(), P, sm, return_lse=True)
+    out, lse = tv.verify_attn_ex(torch.from_numpy(q_lat).cuda(), torch.from_numpy(q_rope).cuda(), _cache(c_kv, dt),
+                                 _cache(k_rope, dt), torch.from_numpy(parent).cuda(), P, sm, flags, return_lse=True)
     torch.cuda.synchronize()
     hs = list(heads)
     ref_out, ref_lse = O.verify_attn(O.as_f64(q_lat[:, :, hs], "f32"), O.as_f64(q_rope[:, :, hs], "f32"),
@@ -71,7 +74,7 @@ def test_long_prefix(case):
     got = out.cpu().numpy()[:, :, hs].astype(np.float64)
     e = errors(got, ref_out)
     el = float(np.max(np.abs(lse.cpu().numpy()[:, :, hs] - ref_lse)))
-    print(f"DRIFT dtype={dt} P={P} B={B} H={H} q={q} heads={hs} max_abs={e['max_abs']:.3e} "
+    print(f"DRIFT dtype={dt} flags={flags} P={P} B={B} H={H} q={q} heads={hs} max_abs={e['max_abs']:.3e} "
           f"max_rel={e['max_rel']:.3e} lse_abs={el:.2e}", flush=True)
     assert e["max_rel"] <= TOL[dt]["max_rel"], e
     if "max_abs" in TOL[dt]:
