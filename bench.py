@@ -370,9 +370,10 @@ def fp32_configs(torch, tv, W, with_oracle: bool = False) -> dict:
 
 def verify_variants(torch, tv, W) -> dict:
     """The verify attention beyond the serving batch: a long prefix with one
-    request, a ragged batch of mixed prefixes and tree sizes, and a 256-node
-    tree.  Synthetic bf16 caches (N(0,1) x 0.5), branching trees; flops counted
-    on the visible (row, key) pairs."""
+    request, a ragged batch of mixed prefixes and tree sizes, a 256-node tree
+    (synthetic bf16 caches, N(0,1) x 0.5), and 8 trees of the serving shape
+    with an fp32 cache (N(0,1)); branching trees; flops counted on the
+    visible (row, key) pairs."""
     import numpy as np
     dev = "cuda:0"
     H, d_c, d_r = 64, 512, 64
@@ -424,6 +425,26 @@ def verify_variants(torch, tv, W) -> dict:
                                                        out=o, workspace=ws), 20, warmup=5)
     flops = H * sum(visible_pairs(p_, P) for p_, P in zip(pars, prefixes)) * (2 * (d_c + d_r) + 2 * d_c)
     out["ragged_b32_q9to33_p2kto16k"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    del q_lat, q_rope, c_kv, k_rope, o, ws
+    # The fp32 cache at the serving batch's per-tree shape (8 trees): the
+    # fp32 matrix-core kernel's 64-row form with every CU busy, against the
+    # fp32 peak.
+    B, q, P = 8, 33, 8192
+    q_lat = torch.randn(B, q, H, d_c, device=dev, generator=g)
+    q_rope = torch.randn(B, q, H, d_r, device=dev, generator=g)
+    c_kv = torch.randn(B, P + q, d_c, device=dev, generator=g)
+    k_rope = torch.randn(B, P + q, d_r, device=dev, generator=g)
+    par = np.stack([W.tree_branch(q, rng) for _ in range(B)]).astype(np.int32)
+    parent = torch.from_numpy(par).to(dev)
+    o = torch.empty_like(q_lat)
+    ws = torch.empty(max(tv.workspace_size(B, H, q, P, d_c, d_r, tv.TV_F32), 1), dtype=torch.uint8, device=dev)
+    ms = _time_ms(torch, lambda: tv.verify_attn(q_lat, q_rope, c_kv, k_rope, parent, P, sm, out=o, workspace=ws),
+                  10, warmup=3)
+    flops = H * sum(visible_pairs(par[b], P) for b in range(B)) * (2 * (d_c + d_r) + 2 * d_c)
+    tf = flops / (ms * 1e-3) / 1e12
+    out["fp32_b8_h64_p8192_q33"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                    "frac_of_fp32_peak": round(tf / PEAKS_TFLOPS["f32_mfma"], 4),
+                                    "kernel": "attn_mfma_f32_kernel"}
     return out
 
 
